@@ -1,0 +1,23 @@
+"""Plain fp64 CPU oracle for paged-KV decode attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+link this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library (no kernels, headers, helpers or constants) and imports nothing from
+``paged_kv_decode_pa_amd``.
+
+Every function is pinned by ``tests/test_oracle_*.py`` against closed forms,
+invariants, a library routine and brute force; no function here is "parity
+unpinned".
+"""
+from .paged_attention import (  # noqa: F401
+    attention,
+    bf16_bits_to_float64,
+    cache_write,
+    combine_partitions,
+    decode,
+    decode_partials,
+    gather_sequence,
+    partition_attention,
+    to_float64,
+)
