@@ -1,0 +1,323 @@
+#!/usr/bin/env python3
+"""Benchmark one paged-KV decode step on one MI355X.
+
+A step is the whole hot path for one batch: pa_reshape_and_cache appends each
+sequence's new token to the page pool, pa_decode attends over every cached
+token, and pa_decode_reduce merges split-KV partitions.  Inputs are synthetic
+(seeded, N(0,1) values cast to bf16) and resident in HBM before timing.  Before
+each timed step a 1 GiB buffer is zeroed on the same stream, outside the timed
+events, so the KV pages come from HBM and not from L2 or the 256 MB
+MALL.
+
+Prints ONE JSON line (the headline workload) on stdout; with --all, lines for
+the other workloads go to stderr first.
+
+    python bench.py [--steps K] [--warmup W] [--config 2] [--all]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: achieved KV HBM GB/s (% of peak) + seqs/sec, 1 GPU"
+PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, vendor peak
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["paged_kv_decode_pa_amd/csrc/decode_mfma.hip",
+                  "paged_kv_decode_pa_amd/csrc/pa_device.hpp"]
+
+WORKLOAD_NAMES = {
+    1: "tiny fp32 decode: 4 seqs, lengths {17,64,100,255}, 8 q / 2 kv heads, D=64, 16-token pages",
+    2: "Llama-3-8B-shaped decode batch: 64 seqs, 32 q / 8 kv heads, D=128, bf16 KV, "
+       "16-token pages, lengths U[512,4096], pages scattered in a 1.25x pool",
+    3: "prefix-reuse decode: 128 seqs in 8 groups of 16 sharing a 2048-token prefix, suffixes "
+       "U[64,512], 32 q / 8 kv heads, D=128, bf16 KV, 16-token pages",
+    4: "long-context split-KV decode: 8 seqs, lengths U[16384,32768], 32 q / 8 kv heads, "
+       "D=128, bf16 KV, 16-token pages, 512-token partitions",
+    5: "70B tensor-parallel-8 per-GPU share: 256 seqs, 8 q / 1 kv head, D=128, bf16 KV, "
+       "16-token pages, lengths log-uniform [128,8192] with 25% at <= 32",
+}
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--all", action="store_true", help="also run the other four workloads")
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="split-KV partition in tokens (default: the workload's own)")
+    ap.add_argument("--kernel", choices=["auto", "valu"], default="auto",
+                    help="auto = pa_decode; valu = pa_decode_valu")
+    ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="time budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (counter calibration)")
+    return ap.parse_args()
+
+
+def stats(xs):
+    a = np.asarray(xs, dtype=np.float64)
+    return {"mean": float(a.mean()), "median": float(np.median(a)),
+            "p10": float(np.percentile(a, 10)), "p90": float(np.percentile(a, 90))}
+
+
+def byte_counts(wl, partition_size):
+    """Algorithmic bytes of one step, from the workload's shapes."""
+    esz = wl.elem_bytes
+    B, Hq, Hkv, D = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    L = wl.context_lens.astype(np.int64)
+    per_token = 2 * Hkv * D * esz                      # K and V rows of one token
+    unique_tokens = len(wl.prefill_slots) + int((wl.new_slots >= 0).sum())
+    kv_unique = unique_tokens * per_token              # shared prefix pages counted once
+    kv_logical = int(L.sum()) * per_token
+    q_bytes = B * Hq * D * esz
+    tables = int(((L + 15) // 16).sum()) * 4 + B * 4
+    n_parts = (L + partition_size - 1) // partition_size if partition_size else np.zeros_like(L)
+    partial = int(n_parts.sum()) * Hq * (D + 2) * 4
+    decode = kv_unique + q_bytes + tables + (partial if partition_size else q_bytes)
+    reduce = (partial + q_bytes + B * 4) if partition_size else 0
+    cache_write = B * (2 * per_token + 8)              # read the new rows, write them, slots
+    return {"kv_unique": kv_unique, "kv_logical": kv_logical, "decode_kernel": decode,
+            "reduce_kernel": reduce, "cache_write": cache_write,
+            "step": decode + reduce + cache_write}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(cid, partition_size):
+    """HBM bytes per decode launch from a committed counter summary, or None
+    when the summary is absent or the kernel changed since it was taken."""
+    path = os.path.join(PROFILES, f"traffic_decode_mfma_cfg{cid}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    if int(kv.get("partition_size", -1)) != partition_size:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def run_config(cid, args, headline):
+    import torch
+
+    import paged_kv_decode_pa_amd as pa
+    from workloads import config_by_id, make_workload
+
+    cfg = config_by_id(cid)
+    ps = cfg.bench_partition_size if args.partition_size is None else args.partition_size
+    t0 = time.time()
+    wl = make_workload(cfg)
+    print(f"[bench] config {cid} ({cfg.name}) drawn in {time.time() - t0:.1f}s; "
+          f"partition {ps}", file=sys.stderr, flush=True)
+
+    dev = torch.device("cuda:0")
+    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+
+    def up(a):
+        if wl.dtype == "f32":
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    P, Hkv, D, Hq, B = wl.page_size, wl.num_kv_heads, wl.head_dim, wl.num_q_heads, wl.num_seqs
+    k_cache = torch.full((wl.num_pages, Hkv, P, D), float("nan"), dtype=dt, device=dev)
+    v_cache = torch.full((wl.num_pages, Hkv, D, P), float("nan"), dtype=dt, device=dev)
+    pa.pa_reshape_and_cache(up(wl.prefill_key), up(wl.prefill_value), k_cache, v_cache,
+                            torch.from_numpy(wl.prefill_slots).to(dev))
+    query = up(wl.query)
+    new_key, new_value = up(wl.new_key), up(wl.new_value)
+    new_slots = torch.from_numpy(wl.new_slots).to(dev)
+    tables = torch.from_numpy(wl.block_tables).to(dev)
+    lens = torch.from_numpy(wl.context_lens).to(dev)
+    out = torch.empty((B, Hq, D), dtype=dt, device=dev)
+    n_parts = max(1, -(-int(wl.context_lens.max()) // ps)) if ps else 0
+    po = torch.empty((B, Hq, n_parts, D), dtype=torch.float32, device=dev) if ps else None
+    pm = torch.empty((B, Hq, n_parts), dtype=torch.float32, device=dev) if ps else None
+    psum = torch.empty((B, Hq, n_parts), dtype=torch.float32, device=dev) if ps else None
+    decode_fn = pa.pa_decode if args.kernel == "auto" else pa.pa_decode_valu
+    flush_buf = None if args.no_flush else torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        pa.pa_reshape_and_cache(new_key, new_value, k_cache, v_cache, new_slots)
+        if ev:
+            ev[1].record()
+        if ps:
+            decode_fn(None, query, k_cache, v_cache, tables, lens, wl.scale, ps, po, pm, psum)
+        else:
+            decode_fn(out, query, k_cache, v_cache, tables, lens, wl.scale)
+        if ev:
+            ev[2].record()
+        if ps:
+            pa.pa_decode_reduce(out, po, pm, psum, lens, ps)
+        if ev:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        if flush_buf is not None:
+            flush_buf.zero_()
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for k in range(args.steps):
+        if flush_buf is not None:
+            flush_buf.zero_()
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    if not torch.isfinite(out.float()).all():
+        raise RuntimeError("non-finite decode output")
+
+    step_ms = [e[0].elapsed_time(e[3]) for e in events]
+    cache_ms = [e[0].elapsed_time(e[1]) for e in events]
+    decode_ms = [e[1].elapsed_time(e[2]) for e in events]
+    reduce_ms = [e[2].elapsed_time(e[3]) for e in events]
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 27, dtype=torch.float32, device=dev).fill_(1.0)  # 512 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    nb = byte_counts(wl, ps)
+    t_step = float(np.mean(step_ms)) * 1e-3
+    t_dec = float(np.mean(decode_ms)) * 1e-3
+    gbs = nb["kv_unique"] / t_step / 1e9
+    achieved = nb["decode_kernel"] / t_dec / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD_NAMES[cid],
+            "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "page_size": P,
+            "partition_size": ps, "kernel": "pa_decode" if args.kernel == "auto" else
+            "pa_decode_valu", "cache_flush_between_steps": flush_buf is not None,
+            "parallelism": "none (1 GPU)",
+        },
+        "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "seqs_per_s": round(B / t_step, 1),
+        "effective_logical_kv_gbs": round(nb["kv_logical"] / t_step / 1e9, 1),
+        "kernels_ms": {"cache_write": stats(cache_ms), "decode": stats(decode_ms),
+                       "reduce": stats(reduce_ms), "step": stats(step_ms)},
+        "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
+        "bytes": nb,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_mfma_kernel" if (wl.dtype == "bf16" and args.kernel == "auto")
+            else "decode_valu_kernel",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": read_traffic(cid, ps) if (wl.dtype == "bf16" and args.kernel == "auto")
+            else None,
+            "algorithmic_bytes_per_launch": nb["decode_kernel"],
+            "mean_launch_us": round(t_dec * 1e6, 2),
+        },
+    }
+    if headline and not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, nb, t_step)
+    return line
+
+
+def cpu_baseline(wl, budget_s, nb, t_step_gpu):
+    """The fp64 oracle, as it stands, on a bounded sample of the same batch:
+    whole sequences in batch order until the time budget is spent."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    store = np.float32 if wl.dtype == "f32" else np.uint16
+    nan = np.float32("nan") if wl.dtype == "f32" else 0x7FC0
+    P, Hkv, D = wl.page_size, wl.num_kv_heads, wl.head_dim
+    k = np.full((wl.num_pages, Hkv, P, D), nan, dtype=store)
+    v = np.full((wl.num_pages, Hkv, D, P), nan, dtype=store)
+    k, v = oracle.cache_write(k, v, wl.prefill_key, wl.prefill_value, wl.prefill_slots, P)
+    k, v = oracle.cache_write(k, v, wl.new_key, wl.new_value, wl.new_slots, P)
+    per_token = 2 * wl.num_kv_heads * wl.head_dim * wl.elem_bytes
+    done, tokens, t = 0, 0, 0.0
+    while t < budget_s and done < 50 * wl.num_seqs:
+        b = done % wl.num_seqs
+        t0 = time.perf_counter()
+        oracle.decode(wl.query[b:b + 1], k, v, wl.block_tables[b:b + 1],
+                      wl.context_lens[b:b + 1], wl.scale, wl.page_size, wl.dtype)
+        t += time.perf_counter() - t0
+        tokens += int(wl.context_lens[b])
+        done += 1
+    gbs = tokens * per_token / t / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} sequence decodes cycling through the same {wl.num_seqs}-sequence "
+                      f"batch in order ({tokens} cached tokens attended), fp64 NumPy, "
+                      f"{t:.1f}s of CPU time",
+            "seqs_per_s": round(done / t, 2),
+            "host_cpus_visible": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(decode attention shards by sequence or kv head with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import paged_kv_decode_pa_amd as pa
+
+    pa.load()
+    others = [c for c in (1, 2, 3, 4, 5) if c != args.config] if args.all else []
+    for cid in others:
+        print(json.dumps(run_config(cid, args, headline=False)), file=sys.stderr, flush=True)
+    print(json.dumps(run_config(args.config, args, headline=True)), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,190 @@
+/*
+ * pa.h — paged-KV decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * A plain C ABI: every buffer is a pointer to caller-allocated DEVICE memory,
+ * every size is a plain integer, and the stream is a hipStream_t passed as
+ * void* (NULL = the default stream).  No HIP or framework types appear here.
+ *
+ * The problem, as the source pages frame it:
+ *   - a batch of sequences, each with its own context length (Dragon
+ *     "Inference Service" developer guide, "vLLM Integration": max_num_seqs
+ *     and max_model_len bound the batch and the context);
+ *   - one shared pool of fixed-size KV pages addressed through per-sequence
+ *     block tables (llm-d router blog post, engine metric spec: page_size and
+ *     num_pages; vLLM "EngineCoreClient" page, "Archivos clave":
+ *     num_gpu_blocks and block_size reported as the real cache capacity);
+ *   - pages shared across sequences by prefix reuse (llm-d blog post,
+ *     prefix-cache producer section); the device code only ever reads them;
+ *   - decode attention, named there as paged attention under continuous
+ *     batching and described as memory-bandwidth bound (llm-d blog post,
+ *     opening section and the disaggregated P/D paragraph).
+ *
+ * Pool layout (page_size = 16 tokens, "head-major": a page id selects one
+ * contiguous block holding every kv head, and each (page, kv head) tile is
+ * itself contiguous):
+ *     k_cache[num_pages][num_kv_heads][16][head_dim]     key rows per slot
+ *     v_cache[num_pages][num_kv_heads][head_dim][16]     value columns per slot
+ * Token position t of sequence b is stored at page block_tables[b][t / 16],
+ * in-page slot t % 16.  Element types: float32 or bf16 (PA_DTYPE_*); query,
+ * output, key/value inputs and both pools share one element type.
+ *
+ * Attention (the reading taken of the pages, which never write the formula):
+ *     out[b][h] = sum_{t < L_b} softmax_t(scale * q[b][h] . k[b][t][g]) v[b][t][g]
+ *     with g = h / (num_q_heads / num_kv_heads)   (contiguous GQA groups).
+ * Accumulation is in float32; bf16 outputs are rounded to nearest even.
+ *
+ * Ownership and ordering: the library never allocates, frees or
+ * synchronizes.  Each call validates its arguments on the host, enqueues its
+ * kernels on `stream` and returns; buffers must stay alive and unmodified
+ * until the stream has passed the call (the same lifetime rule the vLLM
+ * EngineCoreClient page describes for tensors in flight, "Archivos clave",
+ * SyncMPClient send path).  Results are deterministic: they depend only on
+ * the logical token order, never on physical page placement or sharing.
+ *
+ * Errors (TensorRT Edge-LLM "HTTP Inference Server Architecture", "Extension
+ * Rules": unsupported options are rejected, never silently ignored):
+ *   PA_ERR_INVALID_ARGUMENT  a NULL pointer, a negative count, or
+ *                            inconsistent sizes; nothing was launched;
+ *   PA_ERR_UNSUPPORTED       head_dim not 64/128, page_size not 16, an
+ *                            unknown dtype, or a GQA group above 16;
+ *                            nothing was launched;
+ *   PA_ERR_LAUNCH            the HIP launch itself failed.
+ * Device data (block-table entries, lengths, slots) is not validated on the
+ * host, since that would need a synchronization.  Kernels skip out-of-range
+ * page ids and slots instead of faulting; the affected outputs are then
+ * unspecified.  Device faults surface asynchronously at the caller's next
+ * synchronization and leave the HIP context unusable (compare the vLLM
+ * EngineCoreClient page, "Límites y fallos": engine death is detected late
+ * and is final).
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARGUMENT = 1,
+  PA_ERR_UNSUPPORTED = 2,
+  PA_ERR_LAUNCH = 3
+} pa_status;
+
+typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype;
+
+#define PA_PAGE_SIZE 16
+#define PA_MAX_GQA_GROUP 16
+
+/*
+ * pa_reshape_and_cache — the slot-mapped cache write.
+ *
+ * For every token t in [0, num_tokens) with slot = slot_mapping[t] >= 0:
+ *     k_cache[slot / 16][h][slot % 16][:]  = key[t][h][:]
+ *     v_cache[slot / 16][h][:][slot % 16]  = value[t][h][:]    for every kv head h.
+ * A negative slot writes nothing (padding tokens).  Slots at or beyond
+ * num_pages * 16 are skipped.  The copy is bit-exact.
+ *
+ *   key, value     [num_tokens][num_kv_heads][head_dim], contiguous.
+ *   k_cache,
+ *   v_cache        the pools, layout above.
+ *   slot_mapping   int64 [num_tokens], device.
+ *
+ * Single writer: non-negative slots must be distinct and must not lie in a
+ * page that another sequence's block table also references (a shared prefix
+ * page is read-only; TensorRT Edge-LLM "HTTP Inference Server
+ * Architecture", "Request Lifecycle": one writer owns retained pages).
+ * Violations give unspecified pool contents.  num_tokens == 0 is a no-op.
+ */
+int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                         const int64_t* slot_mapping, int64_t num_tokens, int num_kv_heads,
+                         int head_dim, int page_size, int64_t num_pages, int dtype,
+                         void* stream);
+
+/*
+ * pa_decode — one query token per sequence attends over its paged context.
+ *
+ *   out            [num_seqs][num_q_heads][head_dim] (dtype); written only
+ *                  when partition_size == 0.
+ *   query          [num_seqs][num_q_heads][head_dim] (dtype).
+ *   k_cache,
+ *   v_cache        the pools, [num_pages] pages, layout above.
+ *   block_tables   int32 [num_seqs][max_pages_per_seq]; entries at and past
+ *                  ceil(L_b / 16) are never read (padding may hold -1).
+ *   context_lens   int32 [num_seqs]; L_b counts every cached token of
+ *                  sequence b, including one appended this step.  0 yields a
+ *                  zero output.  Lengths above 16 * max_pages_per_seq are
+ *                  clamped to it.
+ *   scale          multiplies q . k before the softmax (normally 1/sqrt(D)).
+ *   partition_size 0: single pass, `out` is written directly and the partial
+ *                  buffers may be NULL.  Otherwise a positive multiple of 16:
+ *                  split-KV — the context of every sequence is cut at
+ *                  multiples of partition_size tokens from position 0 and each
+ *                  partition p < ceil(L_b / partition_size) writes
+ *                      partial_max[b][h][p] = m   (a reference score, in
+ *                                                  the units of scale*q.k)
+ *                      partial_sum[b][h][p] = sum_t exp(s_t - m)
+ *                      partial_out[b][h][p][:] = sum_t exp(s_t - m) v_t / partial_sum
+ *                  over its tokens; pa_decode_reduce then produces `out`.
+ *                  m need not be the exact maximum; any reference that keeps
+ *                  the exponentials finite gives the same merged result.
+ *   max_num_partitions  partition dimension of the partial buffers (>= 1 when
+ *                  splitting).  Partitions at or beyond it are not computed.
+ *   partial_out    float32 [num_seqs][num_q_heads][max_num_partitions][head_dim]
+ *   partial_max,
+ *   partial_sum    float32 [num_seqs][num_q_heads][max_num_partitions]
+ *
+ * Requirements: num_q_heads % num_kv_heads == 0, the group
+ * num_q_heads / num_kv_heads <= 16, head_dim in {64, 128}, page_size == 16.
+ * num_seqs == 0 is a no-op.
+ */
+int pa_decode(void* out, const void* query, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+              int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+              int max_pages_per_seq, int64_t num_pages, float scale, int partition_size,
+              int max_num_partitions, float* partial_out, float* partial_max,
+              float* partial_sum, int dtype, void* stream);
+
+/*
+ * pa_decode_valu — pa_decode with the vector-ALU kernel forced.
+ *
+ * Same arguments, layouts, results contract and errors as pa_decode.  For
+ * bf16, pa_decode runs the QK^T and P.V products on the matrix cores with P
+ * rounded to bf16; this variant keeps every product in fp32 on the vector
+ * ALU.  It exists to measure and cross-check the two designs; fp32 pa_decode
+ * already uses it.
+ */
+int pa_decode_valu(void* out, const void* query, const void* k_cache, const void* v_cache,
+                   const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                   int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                   int max_pages_per_seq, int64_t num_pages, float scale, int partition_size,
+                   int max_num_partitions, float* partial_out, float* partial_max,
+                   float* partial_sum, int dtype, void* stream);
+
+/*
+ * pa_decode_reduce — merge split-KV partials by log-sum-exp.
+ *
+ * For every (b, h) with n = min(ceil(L_b / partition_size), max_num_partitions):
+ *     M = max_p partial_max[b][h][p],  w_p = partial_sum[b][h][p] * exp(partial_max[b][h][p] - M)
+ *     out[b][h][:] = sum_p w_p partial_out[b][h][p][:] / sum_p w_p
+ * summed in increasing p; n == 0 writes zeros.  Buffers as in pa_decode;
+ * out is dtype (bf16 rounded to nearest even).
+ */
+int pa_decode_reduce(void* out, const float* partial_out, const float* partial_max,
+                     const float* partial_sum, const int32_t* context_lens, int num_seqs,
+                     int num_q_heads, int head_dim, int partition_size,
+                     int max_num_partitions, int dtype, void* stream);
+
+/* Human-readable name of a pa_status value (static storage). */
+const char* pa_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

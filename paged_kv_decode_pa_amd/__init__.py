@@ -1,0 +1,17 @@
+"""Paged-KV decode attention for MI355X (gfx950): Python face of libpa.so.
+
+The entry points mirror include/pa.h one to one; see ``_lib`` for the
+marshalling.  Build the library with ``python -m paged_kv_decode_pa_amd.build``.
+"""
+from ._lib import (  # noqa: F401
+    LIB_PATH,
+    PAGE_SIZE,
+    PaError,
+    load,
+    pa_decode,
+    pa_decode_reduce,
+    pa_decode_valu,
+    pa_reshape_and_cache,
+    status_string,
+    version,
+)

@@ -1,0 +1,172 @@
+// The C ABI of libpa.so: host-side argument checks, then kernel launches on
+// the caller's stream.  Every check runs before the first HIP call, so a
+// rejected call touches no device state.
+#include <limits.h>
+#include <math.h>
+
+#include "pa.h"
+#include "pa_device.hpp"
+
+namespace pa {
+hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_decode_valu(const DecodeParams& p, int head_dim, bool bf16, hipStream_t stream);
+hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache,
+                                    void* v_cache, const int64_t* slots, int64_t num_tokens,
+                                    int num_kv_heads, int head_dim, int64_t num_pages, bool bf16,
+                                    hipStream_t stream);
+hipError_t launch_decode_reduce(void* out, const float* part_out, const float* part_max,
+                                const float* part_sum, const int32_t* context_lens, int num_seqs,
+                                int num_q_heads, int head_dim, int partition_size, int max_parts,
+                                bool bf16, hipStream_t stream);
+}  // namespace pa
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_common(int head_dim, int page_size, int dtype) {
+  if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (page_size != PA_PAGE_SIZE) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+enum class DecodeKernel { kAuto, kValu };
+
+int decode_impl(DecodeKernel which, void* out, const void* query, const void* k_cache,
+                const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                int max_pages_per_seq, int64_t num_pages, float scale, int partition_size,
+                int max_num_partitions, float* partial_out, float* partial_max,
+                float* partial_sum, int dtype, void* stream) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_pages_per_seq <= 0 ||
+      num_pages <= 0 || partition_size < 0)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (int s = check_common(head_dim, page_size, dtype)) return s;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARGUMENT;
+  const int group = num_q_heads / num_kv_heads;
+  if (group > PA_MAX_GQA_GROUP) return PA_ERR_UNSUPPORTED;
+  if (!query || !k_cache || !v_cache || !block_tables || !context_lens)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(query) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_ERR_INVALID_ARGUMENT;
+  if (!isfinite(scale)) return PA_ERR_INVALID_ARGUMENT;
+  const bool split = partition_size > 0;
+  if (split) {
+    if (partition_size % PA_PAGE_SIZE != 0 || max_num_partitions < 1) return PA_ERR_INVALID_ARGUMENT;
+    if (!partial_out || !partial_max || !partial_sum || !aligned16(partial_out))
+      return PA_ERR_INVALID_ARGUMENT;
+  } else if (!out) {
+    return PA_ERR_INVALID_ARGUMENT;
+  }
+  const int64_t parts = split ? max_num_partitions : 1;
+  const int64_t units = int64_t(num_seqs) * num_kv_heads * parts;
+  if (units > INT_MAX / 2) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+
+  pa::DecodeParams p;
+  p.out = out;
+  p.query = query;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.partial_out = partial_out;
+  p.partial_max = partial_max;
+  p.partial_sum = partial_sum;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = group;
+  p.max_pages_per_seq = max_pages_per_seq;
+  p.num_pages = num_pages;
+  p.scale_log2 = scale * pa::kLog2e;
+  p.pages_per_partition = split ? partition_size / PA_PAGE_SIZE : 0;
+  p.num_partitions = int(parts);
+  p.num_units = int(units);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = dtype == PA_DTYPE_BF16;
+  const hipError_t err = (bf16 && which == DecodeKernel::kAuto)
+                             ? pa::launch_decode_mfma(p, head_dim, s)
+                             : pa::launch_decode_valu(p, head_dim, bf16, s);
+  return err == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                         const int64_t* slot_mapping, int64_t num_tokens, int num_kv_heads,
+                         int head_dim, int page_size, int64_t num_pages, int dtype,
+                         void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_pages <= 0) return PA_ERR_INVALID_ARGUMENT;
+  if (int s = check_common(head_dim, page_size, dtype)) return s;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(key) || !aligned16(k_cache)) return PA_ERR_INVALID_ARGUMENT;
+  if (num_tokens > INT_MAX) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  const hipError_t err = pa::launch_reshape_and_cache(
+      key, value, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim, num_pages,
+      dtype == PA_DTYPE_BF16, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int pa_decode(void* out, const void* query, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+              int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+              int max_pages_per_seq, int64_t num_pages, float scale, int partition_size,
+              int max_num_partitions, float* partial_out, float* partial_max,
+              float* partial_sum, int dtype, void* stream) {
+  return decode_impl(DecodeKernel::kAuto, out, query, k_cache, v_cache, block_tables,
+                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
+                     max_pages_per_seq, num_pages, scale, partition_size, max_num_partitions,
+                     partial_out, partial_max, partial_sum, dtype, stream);
+}
+
+int pa_decode_valu(void* out, const void* query, const void* k_cache, const void* v_cache,
+                   const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                   int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                   int max_pages_per_seq, int64_t num_pages, float scale, int partition_size,
+                   int max_num_partitions, float* partial_out, float* partial_max,
+                   float* partial_sum, int dtype, void* stream) {
+  return decode_impl(DecodeKernel::kValu, out, query, k_cache, v_cache, block_tables,
+                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
+                     max_pages_per_seq, num_pages, scale, partition_size, max_num_partitions,
+                     partial_out, partial_max, partial_sum, dtype, stream);
+}
+
+int pa_decode_reduce(void* out, const float* partial_out, const float* partial_max,
+                     const float* partial_sum, const int32_t* context_lens, int num_seqs,
+                     int num_q_heads, int head_dim, int partition_size, int max_num_partitions,
+                     int dtype, void* stream) {
+  if (num_seqs < 0 || num_q_heads <= 0 || partition_size <= 0 || max_num_partitions < 1)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (int s = check_common(head_dim, PA_PAGE_SIZE, dtype)) return s;
+  if (partition_size % PA_PAGE_SIZE != 0) return PA_ERR_INVALID_ARGUMENT;
+  if (!out || !partial_out || !partial_max || !partial_sum || !context_lens)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (int64_t(num_seqs) * num_q_heads > INT_MAX) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  const hipError_t err = pa::launch_decode_reduce(
+      out, partial_out, partial_max, partial_sum, context_lens, num_seqs, num_q_heads, head_dim,
+      partition_size, max_num_partitions, dtype == PA_DTYPE_BF16,
+      static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARGUMENT: return "PA_ERR_INVALID_ARGUMENT";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH";
+    default: return "PA_ERR_UNKNOWN";
+  }
+}
+
+int pa_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,159 @@
+// Device-side pieces shared by the decode kernels: launch parameters, the
+// work-unit schedule and the cross-wave log-sum-exp merge.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kPage = 16;          // tokens per KV page
+constexpr int kWaves = 4;          // waves per workgroup; each owns every 4th page
+constexpr int kBlock = 64 * kWaves;
+constexpr int kMaxGroup = 16;      // query heads per kv head the kernels accept
+constexpr int kXcds = 8;           // MI355X: 8 XCDs, workgroups dealt round-robin
+constexpr int kUnitTile = 16;      // consecutive units kept on one XCD
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct DecodeParams {
+  void* out;
+  const void* query;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* partial_out;
+  float* partial_max;
+  float* partial_sum;
+  int num_seqs;
+  int num_q_heads;
+  int num_kv_heads;
+  int group;                // num_q_heads / num_kv_heads
+  int max_pages_per_seq;
+  int64_t num_pages;
+  float scale_log2;         // scale * log2(e): scores are kept in base-2 units
+  int pages_per_partition;  // 0: the whole context is one unit
+  int num_partitions;       // partitions per (sequence, kv head) in the grid
+  int num_units;            // num_kv_heads * num_partitions * num_seqs
+};
+
+// Number of workgroups covering every unit under unit_of_block's schedule.
+__host__ __device__ inline int decode_grid(int num_units) {
+  const int tiles = (num_units + kUnitTile - 1) / kUnitTile;
+  const int rounds = (tiles + kXcds - 1) / kXcds;
+  return rounds * kXcds * kUnitTile;
+}
+
+// Work unit u enumerates (kv head, partition, sequence) with the sequence
+// fastest, so consecutive units read the same pages when neighbouring
+// sequences share a prefix.  Units are cut into tiles of kUnitTile; tile k
+// goes to XCD k % 8, so a tile's sequences meet in one XCD's L2 while the
+// tiles themselves stay spread evenly over the XCDs.
+__device__ inline bool unit_of_block(const DecodeParams& p, int& seq, int& kvh, int& part) {
+  const int blk = blockIdx.x;
+  const int xcd = blk % kXcds;
+  const int j = blk / kXcds;
+  const int tile = (j / kUnitTile) * kXcds + xcd;
+  const int u = tile * kUnitTile + j % kUnitTile;
+  if (u >= p.num_units) return false;
+  seq = u % p.num_seqs;
+  const int rest = u / p.num_seqs;
+  part = rest % p.num_partitions;
+  kvh = rest / p.num_partitions;
+  return true;
+}
+
+// Page range [lo, hi) of a unit; false when the unit has no tokens.
+__device__ inline bool unit_pages(const DecodeParams& p, int seq, int part, int L, int& lo,
+                                  int& hi) {
+  int n = (L + kPage - 1) / kPage;
+  if (n > p.max_pages_per_seq) n = p.max_pages_per_seq;
+  if (p.pages_per_partition > 0) {
+    lo = part * p.pages_per_partition;
+    hi = min(lo + p.pages_per_partition, n);
+  } else {
+    lo = 0;
+    hi = n;
+  }
+  return lo < hi;
+}
+
+__device__ inline float bf16_to_f32(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
+
+__device__ inline uint16_t f32_to_bf16(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));  // round to nearest even
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ static void store(void* base, size_t i, float v) { static_cast<float*>(base)[i] = v; }
+};
+template <> struct Elem<uint16_t> {
+  __device__ static void store(void* base, size_t i, float v) {
+    static_cast<uint16_t*>(base)[i] = f32_to_bf16(v);
+  }
+};
+
+// LDS used by the merge: per wave a reference max and a sum per head, and
+// the un-normalised accumulator [wave][head][dim] for the group's heads.
+__host__ __device__ inline size_t merge_lds_bytes(int group, int head_dim) {
+  return sizeof(float) * (2 * kWaves * kMaxGroup + size_t(kWaves) * group * head_dim);
+}
+
+struct MergeLds {
+  float* m;    // [kWaves][kMaxGroup]  base-2 reference score
+  float* l;    // [kWaves][kMaxGroup]  sum of 2^(s - m)
+  float* acc;  // [kWaves][group][D]
+  __device__ MergeLds(float* smem) : m(smem), l(smem + kWaves * kMaxGroup),
+                                     acc(smem + 2 * kWaves * kMaxGroup) {}
+};
+
+// Combine the four waves' online-softmax states of one unit (fixed wave
+// order, so the result is deterministic) and store either the final output
+// or the unit's split-KV partial.  Every thread of the block must call it.
+template <typename OutT, int D>
+__device__ inline void merge_and_store(const DecodeParams& p, const MergeLds& s, int seq, int kvh,
+                                       int part) {
+  __syncthreads();
+  const int G = p.group;
+  for (int idx = threadIdx.x; idx < G * D; idx += kBlock) {
+    const int h = idx / D;
+    const int d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s.m[w * kMaxGroup + h]);
+    float wsum = 0.f, num = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = s.m[w * kMaxGroup + h];
+      const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      wsum += s.l[w * kMaxGroup + h] * f;
+      num += s.acc[(w * G + h) * D + d] * f;
+    }
+    const float o = wsum > 0.f ? num / wsum : 0.f;
+    const int qh = kvh * G + h;
+    if (p.pages_per_partition == 0) {
+      Elem<OutT>::store(p.out, (size_t(seq) * p.num_q_heads + qh) * D + d, o);
+    } else {
+      const size_t row = (size_t(seq) * p.num_q_heads + qh) * p.num_partitions + part;
+      p.partial_out[row * D + d] = o;
+      if (d == 0) {
+        p.partial_max[row] = M * kLn2;  // natural-log units of scale * q.k
+        p.partial_sum[row] = wsum;
+      }
+    }
+  }
+}
+
+// Zero output rows of a unit with an empty context (single pass only).
+template <typename OutT, int D>
+__device__ inline void store_zeros(const DecodeParams& p, int seq, int kvh) {
+  const int G = p.group;
+  for (int idx = threadIdx.x; idx < G * D; idx += kBlock) {
+    const int qh = kvh * G + idx / D;
+    Elem<OutT>::store(p.out, (size_t(seq) * p.num_q_heads + qh) * D + idx % D, 0.f);
+  }
+}
+
+}  // namespace pa

@@ -1,0 +1,172 @@
+"""libpa.so on the CPU: it loads, exports what include/pa.h declares, and
+rejects every host-checkable bad argument before touching the GPU.
+
+No call here reaches a kernel launch: each one either fails validation or is
+an empty batch, both of which return before the first HIP call.
+"""
+import os
+import re
+
+import pytest
+
+import paged_kv_decode_pa_amd as pa
+from paged_kv_decode_pa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+OK, INVAL, UNSUP = _lib.PA_OK, _lib.PA_ERR_INVALID_ARGUMENT, _lib.PA_ERR_UNSUPPORTED
+BF16, F32 = _lib.PA_DTYPE_BF16, _lib.PA_DTYPE_F32
+P = 0x10000  # a non-NULL, 16-byte aligned address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(pa_\w+)\s*\(", text, re.M)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = pa.load()
+    names = declared_functions()
+    assert {"pa_reshape_and_cache", "pa_decode", "pa_decode_reduce"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert pa.version() == 10000
+
+
+def test_status_strings():
+    assert pa.status_string(OK) == "PA_OK"
+    assert pa.status_string(INVAL) == "PA_ERR_INVALID_ARGUMENT"
+    assert pa.status_string(UNSUP) == "PA_ERR_UNSUPPORTED"
+    assert pa.status_string(_lib.PA_ERR_LAUNCH) == "PA_ERR_LAUNCH"
+    assert pa.status_string(99) == "PA_ERR_UNKNOWN"
+
+
+def decode_args(**kw):
+    a = dict(out=P, query=P, k_cache=P, v_cache=P, block_tables=P, context_lens=P, num_seqs=4,
+             num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, max_pages_per_seq=8,
+             num_pages=64, scale=0.088, partition_size=0, max_num_partitions=0,
+             partial_out=None, partial_max=None, partial_sum=None, dtype=BF16, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+DECODE_CASES = [
+    ("null_query", dict(query=None), INVAL),
+    ("null_k_cache", dict(k_cache=None), INVAL),
+    ("null_v_cache", dict(v_cache=None), INVAL),
+    ("null_tables", dict(block_tables=None), INVAL),
+    ("null_lens", dict(context_lens=None), INVAL),
+    ("null_out_single_pass", dict(out=None), INVAL),
+    ("misaligned_query", dict(query=P + 2), INVAL),
+    ("misaligned_pool", dict(k_cache=P + 8), INVAL),
+    ("negative_seqs", dict(num_seqs=-1), INVAL),
+    ("zero_q_heads", dict(num_q_heads=0), INVAL),
+    ("zero_kv_heads", dict(num_kv_heads=0), INVAL),
+    ("heads_not_divisible", dict(num_q_heads=30), INVAL),
+    ("group_above_16", dict(num_q_heads=32, num_kv_heads=1), UNSUP),
+    ("head_dim_96", dict(head_dim=96), UNSUP),
+    ("head_dim_256", dict(head_dim=256), UNSUP),
+    ("page_size_32", dict(page_size=32), UNSUP),
+    ("unknown_dtype", dict(dtype=7), UNSUP),
+    ("zero_max_pages", dict(max_pages_per_seq=0), INVAL),
+    ("zero_pool", dict(num_pages=0), INVAL),
+    ("nan_scale", dict(scale=float("nan")), INVAL),
+    ("inf_scale", dict(scale=float("inf")), INVAL),
+    ("negative_partition", dict(partition_size=-16), INVAL),
+    ("partition_not_page_multiple", dict(partition_size=40, max_num_partitions=4,
+                                          partial_out=P, partial_max=P, partial_sum=P), INVAL),
+    ("split_without_partials", dict(partition_size=512, max_num_partitions=4), INVAL),
+    ("split_zero_max_partitions", dict(partition_size=512, max_num_partitions=0,
+                                        partial_out=P, partial_max=P, partial_sum=P), INVAL),
+    ("split_misaligned_partials", dict(partition_size=512, max_num_partitions=4,
+                                        partial_out=P + 4, partial_max=P, partial_sum=P), INVAL),
+]
+
+
+@pytest.mark.parametrize("fn", ["pa_decode", "pa_decode_valu"])
+@pytest.mark.parametrize("name,kw,want", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+def test_decode_rejects(fn, name, kw, want):
+    assert getattr(pa.load(), fn)(*decode_args(**kw)) == want
+
+
+def test_decode_empty_batch_is_a_noop():
+    lib = pa.load()
+    assert lib.pa_decode(*decode_args(num_seqs=0)) == OK
+    assert lib.pa_decode(*decode_args(num_seqs=0, partition_size=512, max_num_partitions=2,
+                                      partial_out=P, partial_max=P, partial_sum=P, out=None)) == OK
+    # a split call does not need `out`
+    assert lib.pa_decode_valu(*decode_args(num_seqs=0, out=None, partition_size=16,
+                                           max_num_partitions=1, partial_out=P, partial_max=P,
+                                           partial_sum=P)) == OK
+
+
+def cache_args(**kw):
+    a = dict(key=P, value=P, k_cache=P, v_cache=P, slot_mapping=P, num_tokens=8, num_kv_heads=8,
+             head_dim=128, page_size=16, num_pages=64, dtype=BF16, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+CACHE_CASES = [
+    ("null_key", dict(key=None), INVAL),
+    ("null_value", dict(value=None), INVAL),
+    ("null_k_cache", dict(k_cache=None), INVAL),
+    ("null_v_cache", dict(v_cache=None), INVAL),
+    ("null_slots", dict(slot_mapping=None), INVAL),
+    ("misaligned_key", dict(key=P + 2), INVAL),
+    ("negative_tokens", dict(num_tokens=-3), INVAL),
+    ("zero_kv_heads", dict(num_kv_heads=0), INVAL),
+    ("zero_pool", dict(num_pages=0), INVAL),
+    ("head_dim_80", dict(head_dim=80), UNSUP),
+    ("page_size_8", dict(page_size=8), UNSUP),
+    ("unknown_dtype", dict(dtype=3), UNSUP),
+]
+
+
+@pytest.mark.parametrize("name,kw,want", CACHE_CASES, ids=[c[0] for c in CACHE_CASES])
+def test_cache_write_rejects(name, kw, want):
+    assert pa.load().pa_reshape_and_cache(*cache_args(**kw)) == want
+
+
+def test_cache_write_no_tokens_is_a_noop():
+    assert pa.load().pa_reshape_and_cache(*cache_args(num_tokens=0)) == OK
+
+
+def reduce_args(**kw):
+    a = dict(out=P, partial_out=P, partial_max=P, partial_sum=P, context_lens=P, num_seqs=4,
+             num_q_heads=32, head_dim=128, partition_size=512, max_num_partitions=8, dtype=BF16,
+             stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+REDUCE_CASES = [
+    ("null_out", dict(out=None), INVAL),
+    ("null_partial_out", dict(partial_out=None), INVAL),
+    ("null_partial_max", dict(partial_max=None), INVAL),
+    ("null_partial_sum", dict(partial_sum=None), INVAL),
+    ("null_lens", dict(context_lens=None), INVAL),
+    ("negative_seqs", dict(num_seqs=-2), INVAL),
+    ("zero_heads", dict(num_q_heads=0), INVAL),
+    ("zero_partition", dict(partition_size=0), INVAL),
+    ("partition_not_page_multiple", dict(partition_size=100), INVAL),
+    ("zero_max_partitions", dict(max_num_partitions=0), INVAL),
+    ("head_dim_32", dict(head_dim=32), UNSUP),
+    ("unknown_dtype", dict(dtype=2), UNSUP),
+]
+
+
+@pytest.mark.parametrize("name,kw,want", REDUCE_CASES, ids=[c[0] for c in REDUCE_CASES])
+def test_reduce_rejects(name, kw, want):
+    assert pa.load().pa_decode_reduce(*reduce_args(**kw)) == want
+
+
+def test_reduce_empty_batch_is_a_noop():
+    assert pa.load().pa_decode_reduce(*reduce_args(num_seqs=0)) == OK
+
+
+def test_binding_raises_on_error_status():
+    with pytest.raises(pa.PaError) as e:
+        _lib._check("pa_decode", UNSUP)
+    assert e.value.status == UNSUP and "PA_ERR_UNSUPPORTED" in str(e.value)
