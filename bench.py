@@ -5,9 +5,10 @@ A step is the whole hot path for one batch: pa_reshape_and_cache appends each
 sequence's new token to the page pool, pa_decode attends over every cached
 token, and pa_decode_reduce merges split-KV partitions.  Inputs are synthetic
 (seeded, N(0,1) values cast to bf16) and resident in HBM before timing.  Before
-each timed step a 1 GiB buffer is zeroed on the same stream, outside the timed
-events, so the KV pages come from HBM and not from L2 or the 256 MB
-MALL.
+each timed step a 1 GiB buffer is read on the same stream, outside the timed
+events, so the KV pages come from HBM and not from L2 or the 256 MB MALL.  The
+flush reads rather than writes: a write flush leaves up to 256 MB of dirty
+lines in the MALL whose write-back would be charged to the timed kernels.
 
 Prints ONE JSON line (the headline workload) on stdout; with --all, lines for
 the other workloads go to stderr first.
@@ -162,8 +163,12 @@ def run_config(cid, args, headline):
     pm = torch.empty((B, Hq, n_parts), dtype=torch.float32, device=dev) if ps else None
     psum = torch.empty((B, Hq, n_parts), dtype=torch.float32, device=dev) if ps else None
     decode_fn = pa.pa_decode if args.kernel == "auto" else pa.pa_decode_valu
-    flush_buf = None if args.no_flush else torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    flush_buf = None if args.no_flush else torch.zeros(1 << 28, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
+
+    def flush():
+        if flush_buf is not None:
+            flush_buf.sum()  # read 1 GiB: evicts L2 and MALL, leaves no dirty lines
 
     def step(ev=None):
         if ev:
@@ -183,16 +188,14 @@ def run_config(cid, args, headline):
             ev[3].record()
 
     for _ in range(args.warmup):
-        if flush_buf is not None:
-            flush_buf.zero_()
+        flush()
         step()
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for k in range(args.steps):
-        if flush_buf is not None:
-            flush_buf.zero_()
+        flush()
         step(events[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0

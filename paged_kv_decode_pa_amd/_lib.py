@@ -60,6 +60,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         raise RuntimeError(
             f"{path} is missing: build it with `python -m paged_kv_decode_pa_amd.build` "
             "(there is no fallback implementation)")
+    # torch ships its own HIP runtime; loading it first makes libpa.so bind to
+    # that same runtime (one HIP context per process) instead of a second copy.
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(path)
     for name, argtypes in _SIGNATURES.items():
         fn = getattr(lib, name)

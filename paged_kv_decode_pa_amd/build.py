@@ -29,6 +29,9 @@ def command(out: str = LIB) -> list:
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         # packed fp32 vector ops stay off: the kernels are written for scalar fp32
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # matrix-core accumulators in ordinary VGPRs: the online-softmax rescale
+        # multiplies them in place instead of copying through AGPRs
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-Wno-unused-command-line-argument",
         f"-I{INCLUDE}", f"-I{CSRC}",
         *[os.path.join(CSRC, s) for s in SOURCES],

@@ -1,33 +1,40 @@
 // bf16 paged decode on the matrix cores (gfx950).
 //
-// Work unit: one (sequence, kv head, partition).  A workgroup of four waves
-// takes one unit; wave w walks pages lo+w, lo+w+4, ... with its own online
-// softmax, and the four states are merged through LDS at the end.
-//
 // Per 16-token page and kv head, with the grouped query heads as the 16
-// columns of a matrix tile (groups of 4 or 8 are zero-padded to 16):
+// columns of a matrix tile (groups below 16 are zero-padded):
 //   S^T[16 tok][16 heads]  = K[16 tok][D] . Q^T[D][16 heads]
 //                            D/32 x v_mfma_f32_16x16x32_bf16; A = the K page
-//                            tile straight from HBM (each lane a 16-byte
-//                            row chunk), B = the query group, loaded once.
+//                            tile straight from HBM (each lane a 16-byte row
+//                            chunk), B = the query group, loaded once.
 //   online softmax on the S^T accumulator (lane = head r, tokens 4j..4j+3)
 //   O^T[D][16 heads]      += V^T[D][16 tok] . P^T[16 tok][16 heads]
 //                            D/16 x v_mfma_f32_16x16x16_bf16; A = the V page
 //                            tile (stored dim-major, each lane an 8-byte
 //                            chunk of 4 tokens), B = P^T, which is exactly
-//                            the S^T accumulator's lane layout rounded to bf16.
-// The matrix cores turn a page's 2*G*D*16 multiply-adds into 3*D/32 issue
-// slots, so the vector ALU only runs the softmax and the loads dominate.
+//                            the S^T accumulator's lane layout in bf16.
+//   plus one 16x16x16 product of a row of ones with P^T: the softmax
+//   denominator, summed from the same rounded P as the numerator.
+// A page thus costs 3*D/32 + 1 matrix instructions and ~25 vector ones;
+// the loads dominate.
+//
+// Two kernels share that per-page step:
+//   decode_split_kernel  split-KV: one wave per (sequence, partition, kv
+//                        head), streaming the partition's pages and writing
+//                        its partial straight from registers;
+//   decode_whole_kernel  single pass: four waves per (sequence, kv head),
+//                        each taking every fourth page, merged through LDS.
 #include "pa_device.hpp"
 
 namespace pa {
 namespace {
 
+constexpr float kRescaleSlack = 8.0f;   // base 2: P may reach 2^8 before a rescale
+constexpr int kBufferFlags = 0x00020000;  // raw-buffer descriptor word 3, gfx9 family
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int D>
 struct PageTile {
@@ -35,169 +42,276 @@ struct PageTile {
   s16x4 v[D / 16];   // V^T[16db + r][4j .. 4j+3]
 };
 
+// Page tiles are read through buffer descriptors built in scalar registers
+// (base = the tile, range = its bytes; range 0 reads zeros) and a fixed
+// 32-bit per-lane offset, so a page costs no vector address arithmetic.
 template <int D>
-__device__ inline void load_tile(PageTile<D>& t, const uint16_t* kt, const uint16_t* vt, int r,
-                                 int j) {
+__device__ inline void load_tile(PageTile<D>& t, const char* kt, const char* vt, uint32_t nbytes,
+                                 uint32_t koff, uint32_t voff) {
+  const __amdgpu_buffer_rsrc_t kr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kt), 0, nbytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vt), 0, nbytes, kBufferFlags);
 #pragma unroll
   for (int kb = 0; kb < D / 32; ++kb)
-    t.k[kb] = __builtin_bit_cast(bf16x8,
-                                 *reinterpret_cast<const u32x4*>(kt + r * D + 32 * kb + 8 * j));
+    t.k[kb] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 64 * kb, 0, 0));
 #pragma unroll
   for (int db = 0; db < D / 16; ++db)
-    t.v[db] = __builtin_bit_cast(s16x4,
-                                 *reinterpret_cast<const u32x2*>(vt + (16 * db + r) * kPage + 4 * j));
+    t.v[db] = __builtin_bit_cast(s16x4, __builtin_amdgcn_raw_buffer_load_b64(vr, voff + 32 * kPage * db, 0, 0));
 }
 
+// The pages one wave walks: logical pages first, first+step, ... (count of
+// them).  Their ids are fetched 64 at a time into a vector register (lane i
+// = the wave's i-th page) 64 to 128 pages ahead of use, and each tile load is
+// unconditional: the ordinal is clamped, a clamped repeat re-reads a tile
+// already in flight, and only tiles with a valid page id are used.
 template <int D>
-__global__ __launch_bounds__(kBlock) void decode_mfma_kernel(DecodeParams p) {
-  extern __shared__ float smem[];
-  int seq, kvh, part;
-  if (!unit_of_block(p, seq, kvh, part)) return;
-  const int L = p.context_lens[seq];
-  int lo, hi;
-  if (!unit_pages(p, seq, part, L, lo, hi)) {
-    if (p.pages_per_partition == 0) store_zeros<uint16_t, D>(p, seq, kvh);
-    return;
+struct PageStream {
+  const int32_t* table;
+  int first, step, row_end, count;
+  int ids_cur, ids_nxt, chunk;
+  const char* kpool;
+  const char* vpool;
+  int64_t num_pages;
+  int num_kv_heads, kvh;
+  uint32_t koff, voff;
+
+  __device__ int fetch(int c, int lane) const {
+    const int i = first + step * (64 * c + lane);
+    return i < row_end ? table[i] : -1;
   }
+  // Request the first 128 page ids (before the context length is known).
+  __device__ void start(int lane) {
+    ids_cur = fetch(0, lane);
+    ids_nxt = fetch(1, lane);
+    chunk = 0;
+  }
+  __device__ bool issue(PageTile<D>& t, int k, int lane) {
+    const int kk = min(k, count - 1);
+    if ((kk >> 6) != chunk) {
+      chunk = kk >> 6;
+      ids_cur = ids_nxt;
+      ids_nxt = fetch(chunk + 1, lane);
+    }
+    const int page = __builtin_amdgcn_readlane(ids_cur, kk & 63);
+    const bool ok = page >= 0 && page < num_pages;
+    constexpr size_t tile_bytes = size_t(kPage) * D * 2;
+    const size_t base = (size_t(ok ? page : 0) * num_kv_heads + kvh) * tile_bytes;
+    load_tile<D>(t, kpool + base, vpool + base, ok ? uint32_t(tile_bytes) : 0u, koff, voff);
+    return ok && k < count;
+  }
+};
 
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = lane & 15;
-  const int j = lane >> 4;
-  const int G = p.group;
+// One wave's online-softmax attention state for one kv head's query group.
+template <int D>
+struct WaveAttn {
+  bf16x8 qop[D / 32];    // B operand: column r = query head r of the group
+  s16x4 ones;            // A operand of the denominator block
+  f32x4 acc[D / 16 + 1]; // O^T blocks (lane: dims 16db+4j.., head r), then the denominator
+  float m_run;           // base-2 reference score of head r, equal in all 4 lane groups
+  float scale_log2;
+  int j;
 
-  // Query group as the B operand: column r = query head kvh*G + r.
-  bf16x8 qop[D / 32];
-  {
-    const uint16_t* qrow =
-        static_cast<const uint16_t*>(p.query) + (size_t(seq) * p.num_q_heads + kvh * G + r) * D;
+  __device__ void init(const uint16_t* qrow, bool real_head, int r, int j_, float sl2) {
+    j = j_;
+    scale_log2 = sl2;
 #pragma unroll
     for (int kb = 0; kb < D / 32; ++kb) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (r < G) v = *reinterpret_cast<const u32x4*>(qrow + 32 * kb + 8 * j);
+      if (real_head) v = *reinterpret_cast<const u32x4*>(qrow + 32 * kb + 8 * j);
       qop[kb] = __builtin_bit_cast(bf16x8, v);
     }
+    ones = s16x4{0, 0, 0, 0};
+    if (r == 0) ones = s16x4{0x3F80, 0x3F80, 0x3F80, 0x3F80};
+    m_run = -INFINITY;
+#pragma unroll
+    for (int db = 0; db <= D / 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const uint16_t* kpool = static_cast<const uint16_t*>(p.k_cache);
-  const uint16_t* vpool = static_cast<const uint16_t*>(p.v_cache);
-  const int32_t* table = p.block_tables + size_t(seq) * p.max_pages_per_seq;
-  const size_t tile_elems = size_t(kPage) * D;
-
-  float m_run = -INFINITY;  // base-2 running max for head r
-  float l_run = 0.f;        // this lane's share of the softmax denominator
-  f32x4 acc[D / 16];
+  // One page with `valid` tokens of the context (< 16 only on the last page).
+  // m_run is raised only when a score exceeds it by more than kRescaleSlack,
+  // so P stays <= 2^kRescaleSlack and the accumulator rescale (with its
+  // cross-lane max) runs on few pages.
+  __device__ void page(PageTile<D>& t, int valid) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Page ids of this wave's pages, 64 at a time: lane k holds page lo+w+4k.
-  int ids = -1;
-  auto fetch_ids = [&](int first) {
-    const int i = first + 4 * lane;
-    ids = (i < hi) ? table[i] : -1;
-  };
-  auto page_at = [&](int k) { return __builtin_amdgcn_readlane(ids, k & 63); };
-  auto tile_ptrs = [&](int page, const uint16_t*& kt, const uint16_t*& vt) {
-    const bool ok = page >= 0 && page < p.num_pages;
-    const size_t base = (size_t(ok ? page : 0) * p.num_kv_heads + kvh) * tile_elems;
-    kt = kpool + base;
-    vt = vpool + base;
-    return ok;
-  };
-
-  const int first = lo + w;
-  const int count = first < hi ? (hi - first + 3) / 4 : 0;
-  PageTile<D> cur;
-  bool cur_ok = false;
-  if (count > 0) {
-    fetch_ids(first);
-    const uint16_t *kt, *vt;
-    cur_ok = tile_ptrs(page_at(0), kt, vt);
-    load_tile<D>(cur, kt, vt, r, j);
-  }
-  for (int k = 0; k < count; ++k) {
-    // Issue the next page's loads before working on this one.
-    PageTile<D> nxt;
-    bool nxt_ok = false;
-    if (k + 1 < count) {
-      if (((k + 1) & 63) == 0) fetch_ids(first + 4 * (k + 1));
-      const uint16_t *kt, *vt;
-      nxt_ok = tile_ptrs(page_at(k + 1), kt, vt);
-      load_tile<D>(nxt, kt, vt, r, j);
-    }
-    if (cur_ok) {
-      const int i = first + 4 * k;        // logical page index
-      const int valid = L - i * kPage;    // tokens of this page inside the context
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < D / 32; ++kb)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[kb], qop[kb], s, 0, 0, 0);
+    float s2[4];
 #pragma unroll
-      for (int kb = 0; kb < D / 32; ++kb)
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.k[kb], qop[kb], s, 0, 0, 0);
-      float s2[4];
+    for (int e = 0; e < 4; ++e) s2[e] = s[e] * scale_log2;
+    if (valid < kPage) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s2[e] = s[e] * p.scale_log2;
-      if (valid < kPage) {  // the context's last, partly filled page
+      for (int e = 0; e < 4; ++e)
+        if (4 * j + e >= valid) s2[e] = -INFINITY;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (4 * j + e >= valid) s2[e] = -INFINITY;
-#pragma unroll
-        for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (4 * j + e >= valid) cur.v[db][e] = 0;  // unwritten slots may hold NaN
-      }
-      float pm = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
-      pm = fmaxf(pm, __shfl_xor(pm, 16));
+          if (4 * j + e >= valid) t.v[db][e] = 0;  // unwritten slots may hold NaN
+    }
+    const float lm = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
+    if (__ballot(lm > m_run + kRescaleSlack) != 0) {
+      float pm = fmaxf(lm, __shfl_xor(lm, 16));
       pm = fmaxf(pm, __shfl_xor(pm, 32));
       const float m_new = fmaxf(m_run, pm);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
-      s16x4 pb;
-      float psum = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint16_t b16 = f32_to_bf16(__builtin_amdgcn_exp2f(s2[e] - m_new));
-        pb[e] = static_cast<short>(b16);
-        psum += bf16_to_f32(b16);
-      }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        acc[db] *= alpha;
-        acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cur.v[db], pb, acc[db], 0, 0, 0);
-      }
+      for (int db = 0; db <= D / 16; ++db) acc[db] *= alpha;
     }
-    cur = nxt;
-    cur_ok = nxt_ok;
+    s16x4 pb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      pb[e] = static_cast<short>(f32_to_bf16(__builtin_amdgcn_exp2f(s2[e] - m_run)));
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[db], pb, acc[db], 0, 0, 0);
+    acc[D / 16] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pb, acc[D / 16], 0, 0, 0);
   }
 
-  // Per-head denominator: sum the four lane groups' shares.
-  float l_head = l_run + __shfl_xor(l_run, 16);
-  l_head = l_head + __shfl_xor(l_head, 32);
+  // Walk the stream with two tiles in ping-pong: the next page's loads are in
+  // flight while the current page is computed, and no register copy forces
+  // an early wait.  `page0` is the logical index of ordinal 0, `L` the length.
+  __device__ void run(PageStream<D>& ps, int page0, int L, int lane) {
+    if (ps.count <= 0) return;
+    PageTile<D> ta, tb;
+    bool ok_a = ps.issue(ta, 0, lane);
+    for (int k = 0; k < ps.count; k += 2) {
+      const bool ok_b = ps.issue(tb, k + 1, lane);
+      if (ok_a) page(ta, L - (page0 + ps.step * k) * kPage);
+      if (k + 1 >= ps.count) break;
+      ok_a = ps.issue(ta, k + 2, lane);
+      if (ok_b) page(tb, L - (page0 + ps.step * (k + 1)) * kPage);
+    }
+  }
+};
+
+template <int D>
+__device__ inline PageStream<D> make_stream(const DecodeParams& p, int seq, int kvh, int first,
+                                            int step, int row_end, int lane) {
+  PageStream<D> ps;
+  ps.table = p.block_tables + size_t(seq) * p.max_pages_per_seq;
+  ps.first = first;
+  ps.step = step;
+  ps.row_end = row_end;
+  ps.count = 0;
+  ps.kpool = static_cast<const char*>(p.k_cache);
+  ps.vpool = static_cast<const char*>(p.v_cache);
+  ps.num_pages = p.num_pages;
+  ps.num_kv_heads = p.num_kv_heads;
+  ps.kvh = kvh;
+  const int r = lane & 15, j = lane >> 4;
+  ps.koff = uint32_t(r * D + 8 * j) * 2u;        // K row r, dims 8j .. (+32kb per load)
+  ps.voff = uint32_t(r * kPage + 4 * j) * 2u;    // V^T row r, tokens 4j .. (+16 rows per load)
+  ps.start(lane);
+  return ps;
+}
+
+// ---------------------------------------------------------------- split-KV
+// Unit u = one wave: kv head fastest (block b runs on XCD b % 8, so with 8
+// kv heads each XCD owns one kv head and sequences sharing prefix pages read
+// them through one L2), then sequence, then partition (partitions past a
+// short sequence's end come last in dispatch order).
+template <int D>
+__global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
+  const int u = blockIdx.x;
+  if (u >= p.num_units) return;
+  const int kvh = u % p.num_kv_heads;
+  const int rest = u / p.num_kv_heads;
+  const int seq = rest % p.num_seqs;
+  const int part = rest / p.num_seqs;
+  const int lane = threadIdx.x;
+  const int r = lane & 15, j = lane >> 4;
+  const int G = p.group;
+
+  // Issued together before any of them returns: length, page ids, query.
+  const int lo = part * p.pages_per_partition;
+  const int row_end = min(lo + p.pages_per_partition, p.max_pages_per_seq);
+  PageStream<D> ps = make_stream<D>(p, seq, kvh, lo, 1, row_end, lane);
+  const int L = p.context_lens[seq];
+  WaveAttn<D> wa;
+  wa.init(static_cast<const uint16_t*>(p.query) + (size_t(seq) * p.num_q_heads + kvh * G + r) * D,
+          r < G, r, j, p.scale_log2);
+
+  int n = (L + kPage - 1) / kPage;
+  if (n > p.max_pages_per_seq) n = p.max_pages_per_seq;
+  const int hi = min(lo + p.pages_per_partition, n);
+  if (lo >= hi) return;  // partition past the context: nothing to write
+  ps.count = hi - lo;
+  wa.run(ps, lo, L, lane);
+
+  // Partial of this partition: o = acc / l, m in natural-log units, l.
+  const float l = __shfl(wa.acc[D / 16][0], r);  // row 0 of the denominator block
+  if (r < G) {
+    const size_t row = (size_t(seq) * p.num_q_heads + kvh * G + r) * p.num_partitions + part;
+    float* dst = p.partial_out + row * D;
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+      *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * j) = wa.acc[db] * inv;
+    if (j == 0) {
+      p.partial_max[row] = wa.m_run * kLn2;
+      p.partial_sum[row] = l;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- single pass
+// Unit = (sequence, kv head), four waves; wave w takes pages w, w+4, ...
+template <int D>
+__global__ __launch_bounds__(kBlock) void decode_whole_kernel(DecodeParams p) {
+  extern __shared__ float smem[];
+  int seq, kvh, part;
+  if (!unit_of_block(p, seq, kvh, part)) return;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, j = lane >> 4;
+  const int G = p.group;
+
+  PageStream<D> ps = make_stream<D>(p, seq, kvh, w, kWaves, p.max_pages_per_seq, lane);
+  const int L = p.context_lens[seq];
+  WaveAttn<D> wa;
+  wa.init(static_cast<const uint16_t*>(p.query) + (size_t(seq) * p.num_q_heads + kvh * G + r) * D,
+          r < G, r, j, p.scale_log2);
+
+  int lo, hi;
+  if (!unit_pages(p, seq, part, L, lo, hi)) {
+    store_zeros<uint16_t, D>(p, seq, kvh);
+    return;
+  }
+  ps.count = w < hi ? (hi - w + kWaves - 1) / kWaves : 0;
+  wa.run(ps, w, L, lane);
 
   MergeLds lds(smem);
   if (r < G) {
     if (j == 0) {
-      lds.m[w * kMaxGroup + r] = m_run;
-      lds.l[w * kMaxGroup + r] = l_head;
+      lds.m[w * kMaxGroup + r] = wa.m_run;
+      lds.l[w * kMaxGroup + r] = wa.acc[D / 16][0];
     }
 #pragma unroll
     for (int db = 0; db < D / 16; ++db)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) lds.acc[(w * G + r) * D + 16 * db + 4 * j + e] = acc[db][e];
+      for (int e = 0; e < 4; ++e) lds.acc[(w * G + r) * D + 16 * db + 4 * j + e] = wa.acc[db][e];
   }
   merge_and_store<uint16_t, D>(p, lds, seq, kvh, part);
+}
+
+template <int D>
+hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
+  if (p.pages_per_partition > 0) {
+    decode_split_kernel<D><<<dim3(p.num_units), 64, 0, stream>>>(p);
+  } else {
+    const size_t lds = merge_lds_bytes(p.group, D);
+    decode_whole_kernel<D><<<dim3(decode_grid(p.num_units)), kBlock, lds, stream>>>(p);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t stream) {
-  const dim3 grid(decode_grid(p.num_units));
-  const size_t lds = merge_lds_bytes(p.group, head_dim);
-  if (head_dim == 128)
-    decode_mfma_kernel<128><<<grid, kBlock, lds, stream>>>(p);
-  else
-    decode_mfma_kernel<64><<<grid, kBlock, lds, stream>>>(p);
-  return hipGetLastError();
+  return head_dim == 128 ? launch_d<128>(p, stream) : launch_d<64>(p, stream);
 }
 
 }  // namespace pa

@@ -11,8 +11,6 @@ constexpr int kPage = 16;          // tokens per KV page
 constexpr int kWaves = 4;          // waves per workgroup; each owns every 4th page
 constexpr int kBlock = 64 * kWaves;
 constexpr int kMaxGroup = 16;      // query heads per kv head the kernels accept
-constexpr int kXcds = 8;           // MI355X: 8 XCDs, workgroups dealt round-robin
-constexpr int kUnitTile = 16;      // consecutive units kept on one XCD
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -35,32 +33,24 @@ struct DecodeParams {
   float scale_log2;         // scale * log2(e): scores are kept in base-2 units
   int pages_per_partition;  // 0: the whole context is one unit
   int num_partitions;       // partitions per (sequence, kv head) in the grid
-  int num_units;            // num_kv_heads * num_partitions * num_seqs
+  int num_units;            // num_seqs * num_partitions * num_kv_heads
 };
 
-// Number of workgroups covering every unit under unit_of_block's schedule.
-__host__ __device__ inline int decode_grid(int num_units) {
-  const int tiles = (num_units + kUnitTile - 1) / kUnitTile;
-  const int rounds = (tiles + kXcds - 1) / kXcds;
-  return rounds * kXcds * kUnitTile;
-}
+// Number of workgroups: one per work unit.
+__host__ __device__ inline int decode_grid(int num_units) { return num_units; }
 
-// Work unit u enumerates (kv head, partition, sequence) with the sequence
-// fastest, so consecutive units read the same pages when neighbouring
-// sequences share a prefix.  Units are cut into tiles of kUnitTile; tile k
-// goes to XCD k % 8, so a tile's sequences meet in one XCD's L2 while the
-// tiles themselves stay spread evenly over the XCDs.
+// Work unit u enumerates (sequence, partition, kv head) with the kv head
+// fastest.  Workgroups are dispatched round-robin over the 8 XCDs (block b
+// runs on XCD b % 8), so with 8 kv heads (or a multiple) each XCD owns whole
+// kv heads: every XCD gets the same share of every sequence, and all the
+// sequences that share a prefix page read it through one XCD's L2.
 __device__ inline bool unit_of_block(const DecodeParams& p, int& seq, int& kvh, int& part) {
-  const int blk = blockIdx.x;
-  const int xcd = blk % kXcds;
-  const int j = blk / kXcds;
-  const int tile = (j / kUnitTile) * kXcds + xcd;
-  const int u = tile * kUnitTile + j % kUnitTile;
+  const int u = blockIdx.x;
   if (u >= p.num_units) return false;
-  seq = u % p.num_seqs;
-  const int rest = u / p.num_seqs;
+  kvh = u % p.num_kv_heads;
+  const int rest = u / p.num_kv_heads;
   part = rest % p.num_partitions;
-  kvh = rest / p.num_partitions;
+  seq = rest / p.num_partitions;
   return true;
 }
 
