@@ -248,8 +248,8 @@ def run_config(cid, args, headline):
         "bytes": nb,
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_mfma_kernel" if (wl.dtype == "bf16" and args.kernel == "auto")
-            else "decode_valu_kernel",
+            "kernel": ("decode_valu_kernel" if (wl.dtype != "bf16" or args.kernel != "auto")
+                       else "decode_split_kernel" if ps else "decode_whole_kernel") + f"<{D}>",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
