@@ -29,12 +29,12 @@ namespace pa {
 namespace {
 
 constexpr float kRescaleSlack = 8.0f;   // base 2: P may reach 2^8 before a rescale
-constexpr int kBufferFlags = 0x00020000;  // raw-buffer descriptor word 3, gfx9 family
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int D>
 struct PageTile {
@@ -42,29 +42,26 @@ struct PageTile {
   s16x4 v[D / 16];   // V^T[16db + r][4j .. 4j+3]
 };
 
-// Page tiles are read through buffer descriptors built in scalar registers
-// (base = the tile, range = its bytes; range 0 reads zeros) and a fixed
-// 32-bit per-lane offset, so a page costs no vector address arithmetic.
+// Page tiles are read with global loads from a wave-uniform tile base plus
+// a fixed 32-bit per-lane offset.  (Buffer-descriptor loads were measured 6-7%
+// slower on the long-context and prefix-reuse workloads.)
 template <int D>
-__device__ inline void load_tile(PageTile<D>& t, const char* kt, const char* vt, uint32_t nbytes,
-                                 uint32_t koff, uint32_t voff) {
-  const __amdgpu_buffer_rsrc_t kr =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kt), 0, nbytes, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t vr =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vt), 0, nbytes, kBufferFlags);
+__device__ inline void load_tile(PageTile<D>& t, const char* kt, const char* vt, uint32_t koff,
+                                 uint32_t voff) {
 #pragma unroll
   for (int kb = 0; kb < D / 32; ++kb)
-    t.k[kb] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 64 * kb, 0, 0));
+    t.k[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kt + koff + 64 * kb));
 #pragma unroll
   for (int db = 0; db < D / 16; ++db)
-    t.v[db] = __builtin_bit_cast(s16x4, __builtin_amdgcn_raw_buffer_load_b64(vr, voff + 32 * kPage * db, 0, 0));
+    t.v[db] = __builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(vt + voff + 32 * kPage * db));
 }
 
 // The pages one wave walks: logical pages first, first+step, ... (count of
 // them).  Their ids are fetched 64 at a time into a vector register (lane i
 // = the wave's i-th page) 64 to 128 pages ahead of use, and each tile load is
 // unconditional: the ordinal is clamped, a clamped repeat re-reads a tile
-// already in flight, and only tiles with a valid page id are used.
+// already in flight, and only tiles with a valid page id are used (an invalid
+// id loads page 0's tile, which always exists, and is then skipped).
 template <int D>
 struct PageStream {
   const int32_t* table;
@@ -97,7 +94,7 @@ struct PageStream {
     const bool ok = page >= 0 && page < num_pages;
     constexpr size_t tile_bytes = size_t(kPage) * D * 2;
     const size_t base = (size_t(ok ? page : 0) * num_kv_heads + kvh) * tile_bytes;
-    load_tile<D>(t, kpool + base, vpool + base, ok ? uint32_t(tile_bytes) : 0u, koff, voff);
+    load_tile<D>(t, kpool + base, vpool + base, koff, voff);
     return ok && k < count;
   }
 };
@@ -209,21 +206,115 @@ __device__ inline PageStream<D> make_stream(const DecodeParams& p, int seq, int 
 }
 
 // ---------------------------------------------------------------- split-KV
-// Unit u = one wave: kv head fastest (block b runs on XCD b % 8, so with 8
-// kv heads each XCD owns one kv head and sequences sharing prefix pages read
-// them through one L2), then sequence, then partition (partitions past a
-// short sequence's end come last in dispatch order).
+constexpr int kPlanChunks = 16;  // batches up to 1024 sequences use the unit plan
+
+__device__ inline int wave_sum(int v) {
+#pragma unroll
+  for (int x = 1; x < 64; x <<= 1) v += __shfl_xor(v, x);
+  return v;
+}
+
+// Index (within its 64-lane chunk) of the k-th set bit of a wave ballot.
+__device__ inline int kth_set_lane(uint64_t mask, int k, int lane) {
+  const bool set = (mask >> lane) & 1;
+  const int rank = __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32),
+                                             __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0));
+  const uint64_t hit = __ballot(set && rank == k);
+  return hit ? __builtin_ctzll(hit) : -1;
+}
+
+// The split-KV units that hold tokens, enumerated without scratch memory:
+// every wave reads all context lengths and derives the same list.  Per kv
+// head, the full partitions come first in partition-major order (partition 0
+// of every sequence, then partition 1, ...) and each sequence's partly filled
+// last partition comes after all of them, so the longest units are dispatched
+// first and no wave is spent on a partition past a context's end.  Returns
+// false for an index past the last unit.
+__device__ bool split_unit(const DecodeParams& p, int useq, int lane, int& seq, int& part) {
+  const int PP = p.pages_per_partition;
+  const int chunks = (p.num_seqs + 63) / 64;
+  int nfull[kPlanChunks], hasp[kPlanChunks];
+  int full_total = 0, part_total = 0;
+#pragma unroll
+  for (int c = 0; c < kPlanChunks; ++c) {
+    nfull[c] = 0;
+    hasp[c] = 0;
+    if (c < chunks) {
+      const int b = 64 * c + lane;
+      int pages = 0;
+      if (b < p.num_seqs) pages = (max(p.context_lens[b], 0) + kPage - 1) / kPage;
+      pages = min(pages, p.max_pages_per_seq);
+      const int nparts = min((pages + PP - 1) / PP, p.num_partitions);
+      nfull[c] = min(pages / PP, p.num_partitions);
+      hasp[c] = nparts > nfull[c] ? 1 : 0;
+      full_total += nfull[c];
+      part_total += hasp[c];
+    }
+  }
+  full_total = wave_sum(full_total);
+  part_total = wave_sum(part_total);
+  if (useq < full_total) {
+    // Smallest p with sum_b min(nfull_b, p + 1) > useq.
+    int lo = 0, hi = p.num_partitions;  // O(lo) <= useq < O(hi)
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      int o = 0;
+#pragma unroll
+      for (int c = 0; c < kPlanChunks; ++c) o += min(nfull[c], mid);
+      if (wave_sum(o) <= useq) lo = mid; else hi = mid;
+    }
+    int o = 0;
+#pragma unroll
+    for (int c = 0; c < kPlanChunks; ++c) o += min(nfull[c], lo);
+    int k = useq - wave_sum(o);  // rank among the sequences with a full partition lo
+    part = lo;
+#pragma unroll
+    for (int c = 0; c < kPlanChunks; ++c) {
+      const uint64_t m = __ballot(c < chunks && nfull[c] > lo);
+      const int n = __popcll(m);
+      if (k < n && k >= 0) { seq = 64 * c + kth_set_lane(m, k, lane); return true; }
+      k -= n;
+    }
+    return false;
+  }
+  int k = useq - full_total;
+  if (k >= part_total) return false;
+#pragma unroll
+  for (int c = 0; c < kPlanChunks; ++c) {
+    const uint64_t m = __ballot(c < chunks && hasp[c] != 0);
+    const int n = __popcll(m);
+    if (k < n && k >= 0) {
+      seq = 64 * c + kth_set_lane(m, k, lane);
+      part = __builtin_amdgcn_readlane(nfull[c], seq - 64 * c);
+      return true;
+    }
+    k -= n;
+  }
+  return false;
+}
+
+// Unit = one wave.  Block b runs on XCD b % 8 and the kv head is the fastest
+// index, so with 8 kv heads each XCD owns one kv head and sequences sharing
+// prefix pages read them through one L2.
 template <int D>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   const int u = blockIdx.x;
   if (u >= p.num_units) return;
   const int kvh = u % p.num_kv_heads;
-  const int rest = u / p.num_kv_heads;
-  const int seq = rest % p.num_seqs;
-  const int part = rest / p.num_seqs;
+  const int useq = u / p.num_kv_heads;
   const int lane = threadIdx.x;
   const int r = lane & 15, j = lane >> 4;
   const int G = p.group;
+
+  int seq, part;
+  if (p.num_seqs <= 64 * kPlanChunks) {
+    if (!split_unit(p, useq, lane, seq, part)) return;
+  } else {
+    seq = useq % p.num_seqs;  // plain grid: partitions past a context exit below
+    part = useq / p.num_seqs;
+  }
+  seq = __builtin_amdgcn_readfirstlane(seq);
+  part = __builtin_amdgcn_readfirstlane(part);
 
   // Issued together before any of them returns: length, page ids, query.
   const int lo = part * p.pages_per_partition;

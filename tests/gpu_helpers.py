@@ -89,9 +89,10 @@ class DeviceWorkload:
                wl.scale)
         else:
             n = max_parts or self.partition_count(partition_size)
-            po = torch.empty((B, Hq, n, D), dtype=torch.float32, device=DEV)
-            pm = torch.empty((B, Hq, n), dtype=torch.float32, device=DEV)
-            ps = torch.empty((B, Hq, n), dtype=torch.float32, device=DEV)
+            # NaN-filled so a partition the kernel fails to write poisons the result
+            po = torch.full((B, Hq, n, D), float("nan"), dtype=torch.float32, device=DEV)
+            pm = torch.full((B, Hq, n), float("nan"), dtype=torch.float32, device=DEV)
+            ps = torch.full((B, Hq, n), float("nan"), dtype=torch.float32, device=DEV)
             fn(None, self.query, self.k_cache, self.v_cache, self.block_tables,
                self.context_lens, wl.scale, partition_size, po, pm, ps)
             pa.pa_decode_reduce(out, po, pm, ps, self.context_lens, partition_size)

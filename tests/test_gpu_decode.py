@@ -22,8 +22,8 @@ KERNELS = ["auto", "valu"]
 
 def _splits(cid):
     cfg = config_by_id(cid)
-    s = {0, 512, cfg.bench_partition_size}
-    return sorted(x for x in s if x >= 0)
+    s = {0, 512, cfg.bench_partition_size} | ({256, 1024} if cid > 1 else set())
+    return sorted(s)
 
 
 CONFIG_CASES = [(cid, ps, kern) for cid in (1, 2, 3, 4, 5) for ps in _splits(cid)
@@ -179,3 +179,48 @@ def test_matrix_core_and_vector_kernels_agree():
     a = f64_of(dev.decode(256, "auto"))
     b = f64_of(dev.decode(256, "valu"))
     assert np.abs(a - b).max() <= 2 * TOL["bf16"]
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_long_partitions_rotate_page_ids(kernel):
+    """2048-token partitions: one wave walks 128 pages and refreshes its page ids."""
+    say(f"[decode] 2048-token partitions {kernel}")
+    wl = make_custom_workload([5000, 2048, 4111, 17], num_q_heads=16, num_kv_heads=2, head_dim=128,
+                              seed=31)
+    ref = oracle_reference(wl)
+    dev = DeviceWorkload(wl)
+    for ps in (2048, 4096):
+        assert max_err(dev.decode(ps, kernel), ref) <= TOL["bf16"], ps
+
+
+def test_split_plan_with_empty_and_ragged_contexts():
+    """Zero-length contexts, one-page contexts and full partitions in one batch:
+    every partition that holds tokens is computed exactly once."""
+    say("[decode] split plan, ragged batch with empty contexts")
+    lens = [0, 1, 256, 257, 0, 512, 31, 4096, 255, 16, 0, 1000]
+    wl = make_custom_workload([max(x, 1) for x in lens], num_q_heads=8, num_kv_heads=2,
+                              head_dim=128, seed=77)
+    dev = DeviceWorkload(wl)
+    for b, L in enumerate(lens):
+        if L == 0:
+            dev.context_lens[b] = 0
+    ref = oracle_reference(wl)
+    for ps in (16, 256, 512):
+        out = f64_of(dev.decode(ps))
+        for b, L in enumerate(lens):
+            if L == 0:
+                assert (out[b] == 0).all(), (ps, b)
+            else:
+                assert np.abs(out[b] - ref[b]).max() <= TOL["bf16"], (ps, b)
+
+
+def test_split_beyond_planned_batch_size():
+    """More than 1024 sequences: the split kernel falls back to the plain grid."""
+    say("[decode] 1100-sequence batch")
+    rng = np.random.default_rng(5)
+    lens = rng.integers(1, 80, size=1100).tolist()
+    wl = make_custom_workload(lens, num_q_heads=8, num_kv_heads=1, head_dim=128, seed=6)
+    ref = oracle_reference(wl)
+    dev = DeviceWorkload(wl)
+    for ps in (0, 32):
+        assert max_err(dev.decode(ps), ref) <= TOL["bf16"], ps
