@@ -169,7 +169,8 @@ int pa_decode_valu(void* out, const void* query, const void* k_cache, const void
  * For every (b, h) with n = min(ceil(L_b / partition_size), max_num_partitions):
  *     M = max_p partial_max[b][h][p],  w_p = partial_sum[b][h][p] * exp(partial_max[b][h][p] - M)
  *     out[b][h][:] = sum_p w_p partial_out[b][h][p][:] / sum_p w_p
- * summed in increasing p; n == 0 writes zeros.  Buffers as in pa_decode;
+ * with the numerator accumulated in increasing p and the denominator summed
+ * in a fixed tree order (deterministic); n == 0 writes zeros.  Buffers as in pa_decode;
  * out is dtype (bf16 rounded to nearest even).
  */
 int pa_decode_reduce(void* out, const float* partial_out, const float* partial_max,
