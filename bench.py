@@ -61,6 +61,10 @@ def parse_args():
     ap.add_argument("--kernel", choices=["auto", "valu"], default="auto",
                     help="auto = pa_decode; valu = pa_decode_valu")
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured in a HIP graph (reported, not the value)")
+    ap.add_argument("--unshared", action="store_true",
+                    help="prefix-reuse workload with every sequence's prefix in private pages")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -135,8 +139,8 @@ def run_config(cid, args, headline):
     cfg = config_by_id(cid)
     ps = cfg.bench_partition_size if args.partition_size is None else args.partition_size
     t0 = time.time()
-    wl = make_workload(cfg)
-    print(f"[bench] config {cid} ({cfg.name}) drawn in {time.time() - t0:.1f}s; "
+    wl = make_workload(cfg, share_prefix=not args.unshared)
+    print(f"[bench] config {cid} ({cfg.name}{', unshared' if args.unshared else ''}) drawn in {time.time() - t0:.1f}s; "
           f"partition {ps}", file=sys.stderr, flush=True)
 
     dev = torch.device("cuda:0")
@@ -207,6 +211,39 @@ def run_config(cid, args, headline):
     decode_ms = [e[1].elapsed_time(e[2]) for e in events]
     reduce_ms = [e[2].elapsed_time(e[3]) for e in events]
 
+    # Optionally the same step captured once in a HIP graph and replayed, as a
+    # serving loop might run it: two events bracket each replay and the flush
+    # stays outside them.  (On this stack a replay measured about 2 us slower
+    # than the eager launches, so the value stays the eager step.)
+    graph_ms = None
+    if args.graph:
+        cur = torch.cuda.current_stream()
+        side = torch.cuda.Stream()
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            step()
+        cur.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            flush()
+            graph.replay()
+        torch.cuda.synchronize()
+        gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for k in range(args.steps):
+            flush()
+            gev[k][0].record()
+            graph.replay()
+            gev[k][1].record()
+        torch.cuda.synchronize()
+        graph_ms = [a.elapsed_time(b) for a, b in gev]
+        if not torch.isfinite(out.float()).all():
+            raise RuntimeError("non-finite decode output (graph replay)")
+        del graph
+
     if args.copy_calibration:
         src = torch.empty(1 << 27, dtype=torch.float32, device=dev).fill_(1.0)  # 512 MiB
         dst = torch.empty_like(src)
@@ -235,15 +272,17 @@ def run_config(cid, args, headline):
         "config": {
             "workload": WORKLOAD_NAMES[cid],
             "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "page_size": P,
-            "partition_size": ps, "kernel": "pa_decode" if args.kernel == "auto" else
+            "partition_size": ps, "prefix_pages_shared": not args.unshared, "kernel": "pa_decode" if args.kernel == "auto" else
             "pa_decode_valu", "cache_flush_between_steps": flush_buf is not None,
             "parallelism": "none (1 GPU)",
         },
         "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2),
         "seqs_per_s": round(B / t_step, 1),
         "effective_logical_kv_gbs": round(nb["kv_logical"] / t_step / 1e9, 1),
+        "step_timing": "eager launches, HIP events on the library's stream",
         "kernels_ms": {"cache_write": stats(cache_ms), "decode": stats(decode_ms),
                        "reduce": stats(reduce_ms), "step": stats(step_ms)},
+        "graph_step_ms": stats(graph_ms) if graph_ms else None,
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
         "bytes": nb,
         "roofline": {
@@ -305,7 +344,7 @@ def main():
     args = parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(decode attention shards by sequence or kv head with no exchange; see DESIGN.md)",
+              "(decode attention shards by sequence or kv head with no exchange)",
               file=sys.stderr)
         sys.exit(2)
     import torch

@@ -112,7 +112,13 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
  *   k_cache,
  *   v_cache        the pools, [num_pages] pages, layout above.
  *   block_tables   int32 [num_seqs][max_pages_per_seq]; entries at and past
- *                  ceil(L_b / 16) are never read (padding may hold -1).
+ *                  ceil(L_b / 16) never affect the result (padding may hold
+ *                  -1).  Column 0 of every row is read even when L_b = 0:
+ *                  in batches of up to 1024 sequences, a sequence whose
+ *                  first page also starts another sequence (prefix reuse)
+ *                  has its pages loaded through the caches and every other
+ *                  sequence streams its pages with the nontemporal hint;
+ *                  larger batches load every page through the caches.
  *   context_lens   int32 [num_seqs]; L_b counts every cached token of
  *                  sequence b, including one appended this step.  0 yields a
  *                  zero output.  Lengths above 16 * max_pages_per_seq are

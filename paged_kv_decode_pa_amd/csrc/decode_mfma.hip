@@ -44,24 +44,36 @@ struct PageTile {
 
 // Page tiles are read with global loads from a wave-uniform tile base plus
 // a fixed 32-bit per-lane offset.  (Buffer-descriptor loads were measured 6-7%
-// slower on the long-context and prefix-reuse workloads.)
-template <int D>
+// slower on the long-context and prefix-reuse workloads.)  With Stream set the
+// loads carry the nontemporal hint: a page that no other sequence reads is
+// used once, and keeping it out of the caches' normal replacement measured
+// 8-9% faster on unshared batches.  Pages that several sequences read are
+// loaded normally so that the other readers hit in L2.
+template <bool Stream, typename V>
+__device__ inline V load_vec(const char* ptr) {
+  if constexpr (Stream)
+    return __builtin_nontemporal_load(reinterpret_cast<const V*>(ptr));
+  else
+    return *reinterpret_cast<const V*>(ptr);
+}
+
+template <int D, bool Stream>
 __device__ inline void load_tile(PageTile<D>& t, const char* kt, const char* vt, uint32_t koff,
                                  uint32_t voff) {
 #pragma unroll
   for (int kb = 0; kb < D / 32; ++kb)
-    t.k[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kt + koff + 64 * kb));
+    t.k[kb] = __builtin_bit_cast(bf16x8, load_vec<Stream, u32x4>(kt + koff + 64 * kb));
 #pragma unroll
   for (int db = 0; db < D / 16; ++db)
-    t.v[db] = __builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(vt + voff + 32 * kPage * db));
+    t.v[db] = __builtin_bit_cast(s16x4, load_vec<Stream, u32x2>(vt + voff + 32 * kPage * db));
 }
 
 // The pages one wave walks: logical pages first, first+step, ... (count of
 // them).  Their ids are fetched 64 at a time into a vector register (lane i
-// = the wave's i-th page) 64 to 128 pages ahead of use, and each tile load is
-// unconditional: the ordinal is clamped, a clamped repeat re-reads a tile
-// already in flight, and only tiles with a valid page id are used (an invalid
-// id loads page 0's tile, which always exists, and is then skipped).
+// = the wave's i-th page) 64 to 128 pages ahead of use.  A tile load never
+// depends on the data: the ordinal is clamped to the stream, and an invalid
+// page id loads page 0's tile (which always exists) and reports the tile as
+// not to be used.
 template <int D>
 struct PageStream {
   const int32_t* table;
@@ -83,6 +95,7 @@ struct PageStream {
     ids_nxt = fetch(1, lane);
     chunk = 0;
   }
+  template <bool Stream>
   __device__ bool issue(PageTile<D>& t, int k, int lane) {
     const int kk = min(k, count - 1);
     if ((kk >> 6) != chunk) {
@@ -94,7 +107,13 @@ struct PageStream {
     const bool ok = page >= 0 && page < num_pages;
     constexpr size_t tile_bytes = size_t(kPage) * D * 2;
     const size_t base = (size_t(ok ? page : 0) * num_kv_heads + kvh) * tile_bytes;
-    load_tile<D>(t, kpool + base, vpool + base, koff, voff);
+    // The per-lane offsets pass through an empty asm in place, so each load
+    // is formed as the scalar tile base plus a 32-bit vector offset.
+    // (Otherwise the offsets are folded into 64-bit vector addresses whose
+    // temporaries reuse registers of loads still in flight and force full
+    // memory waits.)
+    asm volatile("" : "+v"(koff), "+v"(voff));
+    load_tile<D, Stream>(t, kpool + base, vpool + base, koff, voff);
     return ok && k < count;
   }
 };
@@ -170,17 +189,43 @@ struct WaveAttn {
   // Walk the stream with two tiles in ping-pong: the next page's loads are in
   // flight while the current page is computed, and no register copy forces
   // an early wait.  `page0` is the logical index of ordinal 0, `L` the length.
-  __device__ void run(PageStream<D>& ps, int page0, int L, int lane) {
-    if (ps.count <= 0) return;
+  // The steady-state loop runs only while all four tiles it touches exist,
+  // so its loads are unconditional and no tile is requested twice (a repeat
+  // would go back to HBM under the nontemporal hint); the last one to three
+  // pages are finished after it.  Only a one-page stream requests a tile
+  // twice (its clamped second request).
+  template <bool Stream>
+  __device__ void walk(PageStream<D>& ps, int page0, int L, int lane) {
+    const int n = ps.count;
+    auto valid = [&](int k) { return L - (page0 + ps.step * k) * kPage; };
     PageTile<D> ta, tb;
-    bool ok_a = ps.issue(ta, 0, lane);
-    for (int k = 0; k < ps.count; k += 2) {
-      const bool ok_b = ps.issue(tb, k + 1, lane);
-      if (ok_a) page(ta, L - (page0 + ps.step * k) * kPage);
-      if (k + 1 >= ps.count) break;
-      ok_a = ps.issue(ta, k + 2, lane);
-      if (ok_b) page(tb, L - (page0 + ps.step * (k + 1)) * kPage);
+    bool ok_a = ps.template issue<Stream>(ta, 0, lane);
+    bool ok_b = ps.template issue<Stream>(tb, 1, lane);  // a one-page stream repeats tile 0
+    int k = 0;
+    for (; k + 3 < n; k += 2) {
+      if (ok_a) page(ta, valid(k));
+      ok_a = ps.template issue<Stream>(ta, k + 2, lane);
+      if (ok_b) page(tb, valid(k + 1));
+      ok_b = ps.template issue<Stream>(tb, k + 3, lane);
     }
+    const int rem = n - k;  // 1 (only when n == 1), 2 or 3 pages left
+    if (ok_a) page(ta, valid(k));
+    if (rem >= 2) {
+      const bool ok_c = rem == 3 && ps.template issue<Stream>(ta, k + 2, lane);
+      if (ok_b) page(tb, valid(k + 1));
+      if (ok_c) page(ta, valid(k + 2));
+    }
+  }
+  // `shared`: some page of this sequence may also be read by another
+  // sequence (cached loads); otherwise the pages stream with the nontemporal
+  // hint.  Its loads were issued with the page ids, which the first tile
+  // needs anyway, so deciding first costs no extra round trip.
+  __device__ void run(PageStream<D>& ps, int page0, int L, int lane, bool shared) {
+    if (ps.count <= 0) return;
+    if (shared)
+      walk<false>(ps, page0, L, lane);
+    else
+      walk<true>(ps, page0, L, lane);
   }
 };
 
@@ -223,36 +268,86 @@ __device__ inline int kth_set_lane(uint64_t mask, int k, int lane) {
   return hit ? __builtin_ctzll(hit) : -1;
 }
 
+// True when sequence `seq` (its first page id is lane seq % 64 of
+// first[seq / 64]; -1 for a sequence with no pages) starts with the same
+// physical page as another sequence of the batch.  Prefix reuse always shares
+// a sequence's first page, so a sequence that passes this test reads no page
+// that another sequence reads.
+template <int NC>
+__device__ inline bool first_page_shared(const int (&first)[NC], int seq) {
+  int f = -1;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    if (c == (seq >> 6)) f = __builtin_amdgcn_readlane(first[c], seq & 63);
+  if (f < 0) return false;
+  int count = 0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) count += __popcll(__ballot(first[c] == f));
+  return count > 1;
+}
+
+// Context length in pages of sequence 64c + lane for c < NC, where NC * 64
+// >= the batch (0 past the batch).  The loads are unconditional (a lane past
+// the batch re-reads the last sequence), so they are all in flight together
+// and the batch costs one memory round trip.
+template <int NC>
+__device__ inline void load_pages(const DecodeParams& p, int lane, int (&pages)[NC]) {
+  int len[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) len[c] = p.context_lens[min(64 * c + lane, p.num_seqs - 1)];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const bool in = 64 * c + lane < p.num_seqs;
+    pages[c] = in ? min((max(len[c], 0) + kPage - 1) / kPage, p.max_pages_per_seq) : 0;
+  }
+}
+
+// First page id of sequence 64c + lane (-1 past the batch or for an empty
+// context), requested for every chunk at once.
+template <int NC>
+struct FirstPages {
+  int len[NC], fid[NC];
+  __device__ void request(const DecodeParams& p, int lane) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int b = min(64 * c + lane, p.num_seqs - 1);
+      len[c] = p.context_lens[b];
+      fid[c] = p.block_tables[size_t(b) * p.max_pages_per_seq];  // column 0 always exists
+    }
+  }
+  __device__ bool shared(const DecodeParams& p, int seq, int lane) const {
+    int first[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      first[c] = (64 * c + lane < p.num_seqs && len[c] > 0) ? fid[c] : -1;
+    return first_page_shared<NC>(first, seq);
+  }
+};
+
 // The split-KV units that hold tokens, enumerated without scratch memory:
 // every wave reads all context lengths and derives the same list.  Per kv
 // head, the full partitions come first in partition-major order (partition 0
 // of every sequence, then partition 1, ...) and each sequence's partly filled
 // last partition comes after all of them, so the longest units are dispatched
 // first and no wave is spent on a partition past a context's end.  Returns
-// false for an index past the last unit.
+// false for an index past the last unit.  NC * 64 >= batch.
+template <int NC>
 __device__ bool split_unit(const DecodeParams& p, int useq, int lane, int& seq, int& part) {
   const int PP = p.pages_per_partition;
-  const int chunks = (p.num_seqs + 63) / 64;
-  int nfull[kPlanChunks], hasp[kPlanChunks];
+  int pages[NC], nfull[NC], hasp[NC];
+  load_pages<NC>(p, lane, pages);
   int full_total = 0, part_total = 0;
 #pragma unroll
-  for (int c = 0; c < kPlanChunks; ++c) {
-    nfull[c] = 0;
-    hasp[c] = 0;
-    if (c < chunks) {
-      const int b = 64 * c + lane;
-      int pages = 0;
-      if (b < p.num_seqs) pages = (max(p.context_lens[b], 0) + kPage - 1) / kPage;
-      pages = min(pages, p.max_pages_per_seq);
-      const int nparts = min((pages + PP - 1) / PP, p.num_partitions);
-      nfull[c] = min(pages / PP, p.num_partitions);
-      hasp[c] = nparts > nfull[c] ? 1 : 0;
-      full_total += nfull[c];
-      part_total += hasp[c];
-    }
+  for (int c = 0; c < NC; ++c) {
+    const int nparts = min((pages[c] + PP - 1) / PP, p.num_partitions);
+    nfull[c] = min(pages[c] / PP, p.num_partitions);
+    hasp[c] = nparts > nfull[c] ? 1 : 0;
+    full_total += nfull[c];
+    part_total += hasp[c];
   }
   full_total = wave_sum(full_total);
   part_total = wave_sum(part_total);
+  seq = -1;
   if (useq < full_total) {
     // Smallest p with sum_b min(nfull_b, p + 1) > useq.
     int lo = 0, hi = p.num_partitions;  // O(lo) <= useq < O(hi)
@@ -260,43 +355,68 @@ __device__ bool split_unit(const DecodeParams& p, int useq, int lane, int& seq, 
       const int mid = (lo + hi) >> 1;
       int o = 0;
 #pragma unroll
-      for (int c = 0; c < kPlanChunks; ++c) o += min(nfull[c], mid);
+      for (int c = 0; c < NC; ++c) o += min(nfull[c], mid);
       if (wave_sum(o) <= useq) lo = mid; else hi = mid;
     }
     int o = 0;
 #pragma unroll
-    for (int c = 0; c < kPlanChunks; ++c) o += min(nfull[c], lo);
+    for (int c = 0; c < NC; ++c) o += min(nfull[c], lo);
     int k = useq - wave_sum(o);  // rank among the sequences with a full partition lo
     part = lo;
 #pragma unroll
-    for (int c = 0; c < kPlanChunks; ++c) {
-      const uint64_t m = __ballot(c < chunks && nfull[c] > lo);
+    for (int c = 0; c < NC; ++c) {
+      const uint64_t m = __ballot(nfull[c] > lo);
       const int n = __popcll(m);
-      if (k < n && k >= 0) { seq = 64 * c + kth_set_lane(m, k, lane); return true; }
+      if (seq < 0 && k < n && k >= 0) seq = 64 * c + kth_set_lane(m, k, lane);
       k -= n;
     }
-    return false;
-  }
-  int k = useq - full_total;
-  if (k >= part_total) return false;
+  } else {
+    int k = useq - full_total;
 #pragma unroll
-  for (int c = 0; c < kPlanChunks; ++c) {
-    const uint64_t m = __ballot(c < chunks && hasp[c] != 0);
-    const int n = __popcll(m);
-    if (k < n && k >= 0) {
-      seq = 64 * c + kth_set_lane(m, k, lane);
-      part = __builtin_amdgcn_readlane(nfull[c], seq - 64 * c);
-      return true;
+    for (int c = 0; c < NC; ++c) {
+      const uint64_t m = __ballot(hasp[c] != 0);
+      const int n = __popcll(m);
+      if (seq < 0 && k < n && k >= 0) {
+        seq = 64 * c + kth_set_lane(m, k, lane);
+        part = __builtin_amdgcn_readlane(nfull[c], seq - 64 * c);
+      }
+      k -= n;
     }
-    k -= n;
   }
-  return false;
+  seq = __builtin_amdgcn_readfirstlane(seq);
+  return seq >= 0;
 }
+
+// Batch-size buckets of the device-side plan and the sharing test: their
+// arrays are sized for NC * 64 sequences, NC in {1, 4, 16}, picked by the
+// host.  NC = 0 (batches above 1024 sequences) does without both: a plain
+// unit grid, and cached loads throughout.
+constexpr int kPlanMaxSeqs = 64 * kPlanChunks;
+
+__host__ __device__ constexpr int plan_chunks_for(int num_seqs) {
+  return num_seqs <= 64 ? 1 : num_seqs <= 256 ? 4 : num_seqs <= kPlanMaxSeqs ? kPlanChunks : 0;
+}
+
+// The sharing test of sequence `seq`: its loads are issued by request(), the
+// answer is read by shared() after other loads have been issued.
+template <int NC>
+struct SharingTest {
+  FirstPages<NC> fp;
+  __device__ void request(const DecodeParams& p, int lane) { fp.request(p, lane); }
+  __device__ bool shared(const DecodeParams& p, int seq, int lane) const {
+    return fp.shared(p, seq, lane);
+  }
+};
+template <>
+struct SharingTest<0> {
+  __device__ void request(const DecodeParams&, int) {}
+  __device__ bool shared(const DecodeParams&, int, int) const { return true; }
+};
 
 // Unit = one wave.  Block b runs on XCD b % 8 and the kv head is the fastest
 // index, so with 8 kv heads each XCD owns one kv head and sequences sharing
 // prefix pages read them through one L2.
-template <int D>
+template <int D, int NC>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   const int u = blockIdx.x;
   if (u >= p.num_units) return;
@@ -307,8 +427,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   const int G = p.group;
 
   int seq, part;
-  if (p.num_seqs <= 64 * kPlanChunks) {
-    if (!split_unit(p, useq, lane, seq, part)) return;
+  if constexpr (NC > 0) {
+    if (!split_unit<NC>(p, useq, lane, seq, part)) return;
   } else {
     seq = useq % p.num_seqs;  // plain grid: partitions past a context exit below
     part = useq / p.num_seqs;
@@ -316,7 +436,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   seq = __builtin_amdgcn_readfirstlane(seq);
   part = __builtin_amdgcn_readfirstlane(part);
 
-  // Issued together before any of them returns: length, page ids, query.
+  // Issued together before any of them returns: the sharing test, length,
+  // page ids, query.
+  SharingTest<NC> sharing;
+  sharing.request(p, lane);
   const int lo = part * p.pages_per_partition;
   const int row_end = min(lo + p.pages_per_partition, p.max_pages_per_seq);
   PageStream<D> ps = make_stream<D>(p, seq, kvh, lo, 1, row_end, lane);
@@ -330,7 +453,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   const int hi = min(lo + p.pages_per_partition, n);
   if (lo >= hi) return;  // partition past the context: nothing to write
   ps.count = hi - lo;
-  wa.run(ps, lo, L, lane);
+  wa.run(ps, lo, L, lane, sharing.shared(p, seq, lane));
 
   // Partial of this partition: o = acc / l, m in natural-log units, l.
   const float l = __shfl(wa.acc[D / 16][0], r);  // row 0 of the denominator block
@@ -372,7 +495,10 @@ __global__ __launch_bounds__(kBlock) void decode_whole_kernel(DecodeParams p) {
     return;
   }
   ps.count = w < hi ? (hi - w + kWaves - 1) / kWaves : 0;
-  wa.run(ps, w, L, lane);
+  // Cached loads throughout: with four waves per unit this kernel runs far
+  // fewer waves than the split one, and the nontemporal hint measured up to
+  // 25% slower here (long contexts of the 256-sequence batch).
+  wa.run(ps, w, L, lane, /*shared=*/true);
 
   MergeLds lds(smem);
   if (r < G) {
@@ -391,7 +517,14 @@ __global__ __launch_bounds__(kBlock) void decode_whole_kernel(DecodeParams p) {
 template <int D>
 hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   if (p.pages_per_partition > 0) {
-    decode_split_kernel<D><<<dim3(p.num_units), 64, 0, stream>>>(p);
+    switch (plan_chunks_for(p.num_seqs)) {
+      case 1: decode_split_kernel<D, 1><<<dim3(p.num_units), 64, 0, stream>>>(p); break;
+      case 4: decode_split_kernel<D, 4><<<dim3(p.num_units), 64, 0, stream>>>(p); break;
+      case kPlanChunks:
+        decode_split_kernel<D, kPlanChunks><<<dim3(p.num_units), 64, 0, stream>>>(p);
+        break;
+      default: decode_split_kernel<D, 0><<<dim3(p.num_units), 64, 0, stream>>>(p); break;
+    }
   } else {
     const size_t lds = merge_lds_bytes(p.group, D);
     decode_whole_kernel<D><<<dim3(decode_grid(p.num_units)), kBlock, lds, stream>>>(p);

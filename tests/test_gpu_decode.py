@@ -224,3 +224,30 @@ def test_split_beyond_planned_batch_size():
     dev = DeviceWorkload(wl)
     for ps in (0, 32):
         assert max_err(dev.decode(ps), ref) <= TOL["bf16"], ps
+
+
+@pytest.mark.parametrize("B", [48, 200, 300])
+def test_scattered_prefix_sharing(B):
+    """Sequences that share prefix pages sit anywhere in the batch, in each
+    batch-size bucket of the device-side plan (up to 64, 256 and 1024
+    sequences).  Sequences that share their first page are read through the
+    caches and the others stream with the nontemporal hint; shared and private
+    copies give identical bits, and both match the oracle."""
+    say(f"[decode] scattered prefix sharing, batch {B}")
+    rng = np.random.default_rng(B)
+    group_of = np.where(rng.random(B) < 0.4, rng.integers(0, 5, B), -1)
+    prefix = 64
+    lens = np.where(group_of >= 0, rng.integers(prefix + 1, 400, B), rng.integers(1, 400, B))
+    kw = dict(num_q_heads=8, num_kv_heads=2, head_dim=128, seed=B, prefix_tokens=prefix,
+              group_of=group_of.tolist())
+    shared = make_custom_workload(lens.tolist(), **kw)
+    private = make_custom_workload(lens.tolist(), share_prefix=False, **kw)
+    firsts = shared.block_tables[:, 0]
+    assert len(np.unique(firsts)) < B  # some first pages are shared ...
+    assert len(np.unique(private.block_tables[:, 0])) == B  # ... and none here
+    ref = oracle_reference(shared)
+    ds, dp = DeviceWorkload(shared), DeviceWorkload(private)
+    for ps in (0, 64, 256):
+        a = ds.decode(ps)
+        assert np.array_equal(bits_of(a), bits_of(dp.decode(ps))), ps
+        assert max_err(a, ref) <= TOL["bf16"], ps

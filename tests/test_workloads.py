@@ -93,3 +93,18 @@ def test_config_table():
     assert [c.config_id for c in CONFIGS] == [1, 2, 3, 4, 5]
     for c in CONFIGS:
         assert c.num_q_heads % c.num_kv_heads == 0 and c.page_size == 16
+
+
+def test_scattered_groups_share_prefix_pages():
+    group_of = [2, -1, 0, 2, 0, -1, 2]
+    lens = [70, 10, 100, 65, 90, 33, 81]
+    wl = make_custom_workload(lens, num_q_heads=4, num_kv_heads=2, head_dim=64, seed=3,
+                              prefix_tokens=64, group_of=group_of)
+    t = wl.block_tables
+    for a, b in [(0, 3), (0, 6), (2, 4)]:
+        assert (t[a, :4] == t[b, :4]).all()
+    assert t[0, 0] != t[2, 0] and t[1, 0] != t[5, 0]
+    assert len(set(t[:, 4].tolist()) - {-1}) == len([x for x in lens if x > 64])
+    private = make_custom_workload(lens, num_q_heads=4, num_kv_heads=2, head_dim=64, seed=3,
+                                   prefix_tokens=64, group_of=group_of, share_prefix=False)
+    assert len(set(private.block_tables[:, 0].tolist())) == len(lens)

@@ -374,6 +374,7 @@ def make_custom_workload(
     pool_factor: float = 1.25,
     pool_pages: Optional[int] = None,
     group_size: int = 0,
+    group_of: Optional[Sequence[int]] = None,
     prefix_tokens: int = 0,
     share_prefix: bool = True,
     placement_seed: Optional[int] = None,
@@ -387,11 +388,16 @@ def make_custom_workload(
 
     ``value_fn(q, k, v, tok_owner, lengths)`` may replace the drawn float32
     values, e.g. to plant a needle token; ``tok_owner[i] = (page_key, position)``.
+    Prefix groups are either contiguous runs of ``group_size`` sequences or
+    given per sequence by ``group_of`` (-1 = no group), in any batch order.
     """
     rng = np.random.default_rng(seed)
     lengths = np.asarray(lengths, dtype=np.int64)
-    group_of = None
-    if group_size:
+    if group_of is not None:
+        group_of = np.asarray(group_of, dtype=np.int64)
+        if group_of.shape != lengths.shape:
+            raise ValueError("group_of needs one entry per sequence")
+    elif group_size:
         group_of = np.arange(len(lengths)) // group_size
     return _build(
         rng, lengths,
