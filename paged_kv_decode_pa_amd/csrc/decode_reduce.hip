@@ -1,21 +1,54 @@
 // Log-sum-exp merge of split-KV partials.  One wave per (sequence, query
 // head): lane k holds partition k's reference score and sum (64 partitions
-// per pass), a wave max gives M, lane k's weight is l_k * exp(m_k - M), and
-// each lane then accumulates D/64 output dims over the partitions in
-// increasing order with the weights broadcast from their lanes.
+// per chunk), a wave max gives M, lane k's weight is l_k * exp(m_k - M), and
+// each lane accumulates D/64 output dims over the partitions in increasing
+// order with the weights broadcast from their lanes.
+//
+// The pass is latency bound (a few loads per row, in dependent steps), so
+// the output rows are read 16 partitions at a time in two register sets in
+// ping-pong, and the first set is requested together with the scores and
+// sums: a row of up to 16 partitions costs one memory round trip, 48
+// partitions three.
 #include "pa_device.hpp"
 
 namespace pa {
 namespace {
 
 constexpr int kReduceWaves = 4;  // (sequence, head) rows per workgroup
-constexpr int kUnroll = 8;       // partitions whose loads are in flight together
+constexpr int kGroup = 16;       // partitions per register set (a chunk holds 64 / kGroup sets)
 
 __device__ inline float wave_max(float v) {
 #pragma unroll
   for (int x = 1; x < 64; x <<= 1) v = fmaxf(v, __shfl_xor(v, x));
   return v;
 }
+
+template <int D>
+struct RowSet {
+  float v[kGroup][D / 64];
+  // Output rows of partitions g*16 .. g*16+15 (clamped to the last one).
+  __device__ void load(const float* o, int g, int n, int lane) {
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) {
+      const float* r = o + size_t(min(g * kGroup + u, n - 1)) * D;
+#pragma unroll
+      for (int i = 0; i < D / 64; ++i) v[u][i] = r[lane + 64 * i];
+    }
+  }
+  // acc += w_t * o_t for the set's partitions below n, in increasing t; the
+  // weight of partition t sits in lane t % 64 of `w`.
+  __device__ void use(float (&acc)[D / 64], float w, int g, int n) const {
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) {
+      const int t = g * kGroup + u;
+      if (t < n) {
+        const float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), t & 63));
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) acc[i] = fmaf(wt, v[u][i], acc[i]);
+      }
+    }
+  }
+};
 
 template <typename OutT, int D>
 __global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_kernel(
@@ -29,43 +62,39 @@ __global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_kernel(
   const int L = context_lens[row / num_q_heads];
   int n = L > 0 ? (L + partition_size - 1) / partition_size : 0;
   if (n > max_parts) n = max_parts;
-  const float* m = part_max + size_t(row) * max_parts;
-  const float* s = part_sum + size_t(row) * max_parts;
-  const float* o = part_out + size_t(row) * max_parts * D;
-
-  // M over all partitions, 64 per pass.
-  float M = -INFINITY;
-  for (int base = 0; base < n; base += 64)
-    M = fmaxf(M, base + lane < n ? m[base + lane] : -INFINITY);
-  M = wave_max(M);
-
   float acc[VD];
 #pragma unroll
   for (int i = 0; i < VD; ++i) acc[i] = 0.f;
   float wsum = 0.f;
-  for (int base = 0; base < n; base += 64) {
-    const int k = base + lane;
-    const float w = k < n ? s[k] * expf(m[k] - M) : 0.f;
-    wsum += w;
-    const int cnt = min(64, n - base);
-    // Eight partitions per step, all loads issued before the first use, so a
-    // long context costs n/8 memory round trips instead of n.
-    for (int t0 = 0; t0 < cnt; t0 += kUnroll) {
-      float v[kUnroll][VD];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const float* ok = o + size_t(base + min(t0 + u, cnt - 1)) * D;
-#pragma unroll
-        for (int i = 0; i < VD; ++i) v[u][i] = ok[lane + 64 * i];
+  if (n > 0) {
+    const float* m = part_max + size_t(row) * max_parts;
+    const float* s = part_sum + size_t(row) * max_parts;
+    const float* o = part_out + size_t(row) * max_parts * D;
+
+    // Requested together: chunk 0's scores and sums, and the first set of rows.
+    RowSet<D> a, b;
+    const float m0 = lane < n ? m[lane] : -INFINITY;
+    const float s0 = lane < n ? s[lane] : 0.f;
+    a.load(o, 0, n, lane);
+    float M = m0;
+    for (int base = 64; base < n; base += 64)
+      M = fmaxf(M, base + lane < n ? m[base + lane] : -INFINITY);
+    M = wave_max(M);
+
+    const int sets = (n + kGroup - 1) / kGroup;
+    float w = 0.f;
+    for (int g = 0; g < sets; g += 2) {
+      if ((g * kGroup) % 64 == 0) {  // first set of a chunk: its weights
+        const int k = g * kGroup + lane;
+        w = k == lane ? (lane < n ? s0 * expf(m0 - M) : 0.f)
+                      : (k < n ? s[k] * expf(m[k] - M) : 0.f);
+        wsum += w;
       }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        if (t0 + u < cnt) {
-          const float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), t0 + u));
-#pragma unroll
-          for (int i = 0; i < VD; ++i) acc[i] = fmaf(wt, v[u][i], acc[i]);
-        }
-      }
+      b.load(o, g + 1, n, lane);
+      a.use(acc, w, g, n);
+      if (g + 1 >= sets) break;
+      if (g + 2 < sets) a.load(o, g + 2, n, lane);
+      b.use(acc, w, g + 1, n);
     }
   }
   // Denominator: lanes hold disjoint partitions; a butterfly sum in a fixed

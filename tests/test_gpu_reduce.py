@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("ps", [16, 64, 512])
 def test_reduce_of_oracle_partials(dtype, ps):
     say(f"[reduce] {dtype} partition {ps}")
-    lens = [1, 16, 17, 511, 512, 513, 3000]
+    lens = [1, 16, 17, 511, 512, 513, 1024, 1040, 3000]  # 64 and 65 partitions of 16
     wl = make_custom_workload(lens, num_q_heads=8, num_kv_heads=2, head_dim=128, dtype=dtype,
                               seed=ps)
     k, v = fill_pools(oracle, wl)
