@@ -1,4 +1,5 @@
-"""Plain fp64 CPU oracle for paged-KV decode attention.
+"""Plain fp64 CPU oracle for paged-KV decode attention (and multi-token
+causal queries over the same cache).
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
 link this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
@@ -14,6 +15,8 @@ from .paged_attention import (  # noqa: F401
     attention,
     bf16_bits_to_float64,
     cache_write,
+    causal_attention,
+    chunk_attention,
     combine_partitions,
     decode,
     decode_partials,

@@ -197,3 +197,61 @@ def decode_partials(query, k_cache, v_cache, block_tables, context_lens, scale,
         ps[b, :, :n] = lsum
         po[b, :, :n] = o
     return po, pm, ps
+
+
+# ------------------------------------------------------- multi-token queries
+# The step on the other side of decode.  The llm-d blog post (the section on
+# the two phases of inference, and the disaggregated-P/D paragraph) separates
+# prefill (compute bound) from decode (memory-bandwidth bound); TensorRT
+# Edge-LLM ("Model Loading") loads an optional draft checkpoint, i.e. several
+# proposed tokens per step that the target model then verifies.  Both run
+# several query tokens of one sequence against its paged cache at once.  The
+# pages give no formula; the plainest reading, taken here, is causal
+# attention: the q_len new tokens of sequence b are its last q_len positions,
+# already written to the cache, and the token at position p attends to
+# positions 0..p.  With q_len = 1 this is exactly :func:`decode`.
+
+
+def causal_attention(q, K, V, scale, positions):
+    """Several query tokens of one sequence, each over the tokens up to and
+    including its own position.
+
+    q: [T][Hq][D]; K and V: [L][Hkv][D] (float64); positions: [T] ints in
+    [0, L).  Query token i is plain :func:`attention` over K[:positions[i] + 1].
+    Returns [T][Hq][D].
+    """
+    T, Hq, D = q.shape
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    for i in range(T):
+        p = int(positions[i])
+        out[i] = attention(q[i], K[:p + 1], V[:p + 1], scale)
+    return out
+
+
+def chunk_attention(query, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                    page_size, dtype):
+    """Multi-token causal attention over paged K/V for a whole batch.
+
+    query: [T][Hq][D] (storage dtype) holds the new tokens of all sequences,
+    sequence b's in rows query_start[b] .. query_start[b + 1] - 1 (so
+    q_len_b = query_start[b + 1] - query_start[b], with q_len_b <= L_b).  Row
+    query_start[b] + i is the token at position L_b - q_len_b + i.  Returns
+    float64 [T][Hq][D]; rows of a sequence with q_len_b = 0 do not exist.
+    """
+    q64 = to_float64(query, dtype)
+    T, Hq, D = q64.shape
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    qs = np.asarray(query_start, dtype=np.int64)
+    for b in range(len(qs) - 1):
+        lo, hi = int(qs[b]), int(qs[b + 1])
+        if hi == lo:
+            continue
+        L = int(context_lens[b])
+        q_len = hi - lo
+        if q_len > L:
+            raise ValueError("more query tokens than context tokens")
+        K, V = gather_sequence(k_cache, v_cache, block_tables[b], L, page_size)
+        positions = np.arange(L - q_len, L)
+        out[lo:hi] = causal_attention(q64[lo:hi], to_float64(K, dtype), to_float64(V, dtype),
+                                      scale, positions)
+    return out

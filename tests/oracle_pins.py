@@ -15,6 +15,10 @@ The independent references used here:
   * invariances of the definition: physical page placement and prefix sharing
     do not change the result; split-KV partials merged by log-sum-exp equal
     the unsplit result.
+For multi-token causal queries (``chunk_attention``): one token per sequence
+is exactly ``decode``; a causal pure-Python brute force over flat offsets;
+torch's attention with an explicit causal offset mask; and causality itself
+(changing a later token's K/V leaves earlier rows bit for bit unchanged).
 """
 from __future__ import annotations
 
@@ -24,7 +28,7 @@ import os
 
 import numpy as np
 
-from workloads import make_custom_workload
+from workloads import make_chunk_queries, make_custom_workload
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_form_decode.json")
 
@@ -106,6 +110,40 @@ def widen(a, dtype):
 def tiny(lengths, Hq=4, Hkv=2, D=8, dtype="f32", seed=0, **kw):
     return make_custom_workload(lengths, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
                                 dtype=dtype, seed=seed, **kw)
+
+
+def brute_force_chunk(wl, kpool, vpool, query, query_start):
+    """Pure-Python causal reference: query row i of sequence b (position
+    L - q_len + i) over that sequence's tokens 0..position, via flat offsets."""
+    Hq, Hkv, D, P = wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.page_size
+    group = Hq // Hkv
+    kflat = widen(kpool, wl.dtype).reshape(-1).tolist()
+    vflat = widen(vpool, wl.dtype).reshape(-1).tolist()
+    q = widen(query, wl.dtype)
+    out = np.zeros((q.shape[0], Hq, D))
+    for b in range(wl.num_seqs):
+        lo, hi = int(query_start[b]), int(query_start[b + 1])
+        L = int(wl.context_lens[b])
+        for r in range(lo, hi):
+            pos = L - (hi - lo) + (r - lo)
+            for h in range(Hq):
+                g = h // group
+                qh = q[r, h].tolist()
+                scores = []
+                for t in range(pos + 1):
+                    page = int(wl.block_tables[b, t // P])
+                    acc = math.fsum(qh[d] * kflat[k_offset(page, g, t % P, d, Hkv, P, D)]
+                                    for d in range(D))
+                    scores.append(wl.scale * acc)
+                mx = max(scores)
+                w = [math.exp(x - mx) for x in scores]
+                z = math.fsum(w)
+                for d in range(D):
+                    num = math.fsum(w[t] * vflat[v_offset(int(wl.block_tables[b, t // P]), g,
+                                                          t % P, d, Hkv, P, D)]
+                                    for t in range(pos + 1))
+                    out[r, h, d] = num / z
+    return out
 
 
 # ---------------------------------------------------------------- checks
@@ -394,6 +432,82 @@ def check_golden(orc):
         assert np.allclose(out[i], np.array(s["expected"]), rtol=0, atol=1e-14), (i, out[i])
 
 
+def check_chunk_single_token_is_decode(orc):
+    wl = tiny([1, 17, 40, 16, 3], Hq=4, Hkv=2, D=8, seed=60)
+    kp, vp = fill_pools(orc, wl)
+    qs = np.arange(wl.num_seqs + 1, dtype=np.int32)
+    got = orc.chunk_attention(wl.query, kp, vp, wl.block_tables, wl.context_lens, qs, wl.scale,
+                              wl.page_size, wl.dtype)
+    want = orc.decode(wl.query, kp, vp, wl.block_tables, wl.context_lens, wl.scale,
+                      wl.page_size, wl.dtype)
+    assert np.array_equal(got, want)
+
+
+def check_chunk_brute_force(orc):
+    cases = [
+        dict(lengths=[1, 17, 40], q=[1, 5, 40], Hq=4, Hkv=2, D=6),
+        dict(lengths=[33, 16], q=[33, 3], Hq=3, Hkv=1, D=5, dtype="bf16"),
+        dict(lengths=[20, 9, 50], q=[0, 9, 7], Hq=2, Hkv=2, D=4),
+    ]
+    for i, c in enumerate(cases):
+        q_lens = c.pop("q")
+        wl = tiny(seed=70 + i, **c)
+        query, qs = make_chunk_queries(wl, q_lens, seed=80 + i)
+        kp, vp = fill_pools(orc, wl)
+        got = orc.chunk_attention(query, kp, vp, wl.block_tables, wl.context_lens, qs,
+                                  wl.scale, wl.page_size, wl.dtype)
+        want = brute_force_chunk(wl, kp, vp, query, qs)
+        assert np.allclose(got, want, rtol=0, atol=1e-12), (i, np.abs(got - want).max())
+
+
+def check_chunk_torch_sdpa(orc):
+    import torch
+
+    wl = tiny([300, 77, 129], Hq=8, Hkv=2, D=32, seed=61)
+    q_lens = [64, 77, 5]
+    query, qs = make_chunk_queries(wl, q_lens, seed=62)
+    kp, vp = fill_pools(orc, wl)
+    got = orc.chunk_attention(query, kp, vp, wl.block_tables, wl.context_lens, qs, wl.scale,
+                              wl.page_size, wl.dtype)
+    q = widen(query, "f32")
+    group = 4
+    for b in range(wl.num_seqs):
+        L, n = int(wl.context_lens[b]), q_lens[b]
+        K = np.zeros((8, L, 32))
+        V = np.zeros((8, L, 32))
+        for t in range(L):
+            page, slot = int(wl.block_tables[b, t // 16]), t % 16
+            for h in range(8):
+                K[h, t] = kp[page, h // group, slot, :]
+                V[h, t] = vp[page, h // group, :, slot]
+        allowed = np.arange(L)[None, :] <= (L - n + np.arange(n))[:, None]   # [n][L]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[qs[b]:qs[b + 1]].transpose(1, 0, 2).copy()),
+            torch.from_numpy(K), torch.from_numpy(V), attn_mask=torch.from_numpy(allowed),
+            scale=wl.scale).numpy().transpose(1, 0, 2)
+        assert np.allclose(got[qs[b]:qs[b + 1]], ref, rtol=0, atol=1e-12), \
+            np.abs(got[qs[b]:qs[b + 1]] - ref).max()
+
+
+def check_chunk_causality(orc):
+    """Changing the K/V of position p leaves every row before p bit for bit
+    unchanged and changes the rows at and after p."""
+    wl = tiny([40], Hq=2, Hkv=1, D=8, seed=63)
+    query, qs = make_chunk_queries(wl, [12], seed=64)     # positions 28..39
+    kp, vp = fill_pools(orc, wl)
+    args = (wl.block_tables, wl.context_lens, qs, wl.scale, wl.page_size, wl.dtype)
+    base = orc.chunk_attention(query, kp, vp, *args)
+    p = 33
+    page, slot = int(wl.block_tables[0, p // 16]), p % 16
+    kp2, vp2 = kp.copy(), vp.copy()
+    kp2[page, 0, slot, :] += 1.0
+    vp2[page, 0, :, slot] -= 2.0
+    moved = orc.chunk_attention(query, kp2, vp2, *args)
+    row_of_p = p - (40 - 12)
+    assert np.array_equal(moved[:row_of_p], base[:row_of_p])
+    assert (np.abs(moved[row_of_p:] - base[row_of_p:]).max(axis=(1, 2)) > 1e-6).all()
+
+
 ALL_CHECKS = [
     check_bf16_widening,
     check_cache_write_layout,
@@ -411,4 +525,8 @@ ALL_CHECKS = [
     check_partitions,
     check_decode_partials,
     check_golden,
+    check_chunk_single_token_is_decode,
+    check_chunk_brute_force,
+    check_chunk_torch_sdpa,
+    check_chunk_causality,
 ]

@@ -111,6 +111,32 @@ def _decode_wrong_row(query, k_cache, v_cache, block_tables, context_lens, scale
     return out
 
 
+def _causal_variant(limit):
+    def causal_attention(q, K, V, scale, positions):
+        T, Hq, D = q.shape
+        out = np.zeros((T, Hq, D))
+        for i in range(T):
+            stop = limit(int(positions[i]), K.shape[0])
+            out[i] = pa.attention(q[i], K[:stop], V[:stop], scale)
+        return out
+    return causal_attention
+
+
+def _chunk_positions_from_zero(query, k_cache, v_cache, block_tables, context_lens, query_start,
+                               scale, page_size, dtype):
+    q64 = pa.to_float64(query, dtype)
+    out = np.zeros(q64.shape)
+    qs = np.asarray(query_start)
+    for b in range(len(qs) - 1):
+        lo, hi = int(qs[b]), int(qs[b + 1])
+        if hi == lo:
+            continue
+        K, V = pa.gather_sequence(k_cache, v_cache, block_tables[b], context_lens[b], page_size)
+        out[lo:hi] = pa.causal_attention(q64[lo:hi], pa.to_float64(K, dtype),
+                                         pa.to_float64(V, dtype), scale, np.arange(hi - lo))
+    return out
+
+
 MUTANTS = {
     "gqa_head_modulo": ("attention", _attention_variant(group_of=lambda h, G, Hkv: h % Hkv)),
     "scale_dropped": ("attention", _attention_variant(use_scale=False)),
@@ -127,6 +153,10 @@ MUTANTS = {
     "partition_ranges_overlap": ("partition_attention", _partition_shifted),
     "bf16_widened_by_15_bits": ("bf16_bits_to_float64", _bf16_shift15),
     "block_table_row_swapped": ("decode", _decode_wrong_row),
+    "chunk_without_causal_mask": ("causal_attention", _causal_variant(lambda p, L: L)),
+    "chunk_excludes_own_token": ("causal_attention", _causal_variant(lambda p, L: max(p, 1))),
+    "chunk_sees_one_token_ahead": ("causal_attention", _causal_variant(lambda p, L: p + 2)),
+    "chunk_positions_from_zero": ("chunk_attention", _chunk_positions_from_zero),
 }
 
 

@@ -108,3 +108,16 @@ def test_scattered_groups_share_prefix_pages():
     private = make_custom_workload(lens, num_q_heads=4, num_kv_heads=2, head_dim=64, seed=3,
                                    prefix_tokens=64, group_of=group_of, share_prefix=False)
     assert len(set(private.block_tables[:, 0].tolist())) == len(lens)
+
+
+def test_chunk_queries_layout_and_bounds():
+    from workloads import make_chunk_queries
+    wl = make_custom_workload([5, 20, 33], num_q_heads=4, num_kv_heads=2, head_dim=8, seed=1)
+    q, qs = make_chunk_queries(wl, [2, 20, 0], seed=3)
+    assert qs.tolist() == [0, 2, 22, 22] and q.shape == (22, 4, 8) and q.dtype == np.uint16
+    q2, _ = make_chunk_queries(wl, [2, 20, 0], seed=3)
+    assert np.array_equal(q, q2)
+    with pytest.raises(ValueError):
+        make_chunk_queries(wl, [6, 1, 1])           # more tokens than the context holds
+    with pytest.raises(ValueError):
+        make_chunk_queries(wl, [1, 1])              # one length per sequence

@@ -11,5 +11,6 @@ from .configs import (  # noqa: F401
     config_by_id,
     make_workload,
     make_custom_workload,
+    make_chunk_queries,
     bf16_bits_from_f32,
 )

@@ -407,3 +407,29 @@ def make_custom_workload(
         placement_rng=None if placement_seed is None else np.random.default_rng(placement_seed),
         max_pages_per_seq=max_pages_per_seq, name=name, scale=scale, value_fn=value_fn,
     )
+
+
+def make_chunk_queries(wl: Workload, q_lens: Sequence[int], seed: int = 0,
+                       value_fn: Optional[Callable] = None):
+    """Query rows for multi-token attention over workload ``wl``'s cache.
+
+    Sequence b gets ``q_lens[b]`` (<= its context length) new query tokens,
+    stored back to back: returns (query [T][Hq][D] payload in wl's dtype,
+    query_start int32 [B + 1]).  The tokens are the sequence's last q_len
+    positions, whose K/V the workload already writes to the pool.  Values are
+    N(0,1) float32 from ``default_rng(seed)``, optionally replaced by
+    ``value_fn(q32, query_start)``.
+    """
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    if q_lens.shape != (wl.num_seqs,):
+        raise ValueError("one query length per sequence")
+    if (q_lens < 0).any() or (q_lens > wl.context_lens).any():
+        raise ValueError("query lengths must lie in [0, context length]")
+    query_start = np.zeros(wl.num_seqs + 1, dtype=np.int32)
+    query_start[1:] = np.cumsum(q_lens)
+    rng = np.random.default_rng(seed)
+    q32 = rng.standard_normal((int(query_start[-1]), wl.num_q_heads, wl.head_dim),
+                              dtype=np.float32)
+    if value_fn is not None:
+        q32 = value_fn(q32, query_start)
+    return _payload(q32, wl.dtype), query_start
