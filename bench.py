@@ -34,7 +34,11 @@ METRIC = "paged decode attention: achieved KV HBM GB/s (% of peak) + seqs/sec, 1
 PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, vendor peak
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["paged_kv_decode_pa_amd/csrc/decode_mfma.hip",
+                  "paged_kv_decode_pa_amd/csrc/page_stream.hpp",
                   "paged_kv_decode_pa_amd/csrc/pa_device.hpp"]
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+CHUNK_METRIC = ("multi-token causal attention over the paged cache (draft verification / "
+                "chunked prefill): query tokens/s, 1 GPU")
 
 WORKLOAD_NAMES = {
     1: "tiny fp32 decode: 4 seqs, lengths {17,64,100,255}, 8 q / 2 kv heads, D=64, 16-token pages",
@@ -70,6 +74,9 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--chunk", type=int, default=0, metavar="Q",
+                    help="time pa_chunk_attention with Q new tokens per sequence instead of the "
+                         "decode step (the cache write of the Q tokens, then the attention)")
     return ap.parse_args()
 
 
@@ -317,6 +324,138 @@ def run_config(cid, args, headline):
     return line
 
 
+def chunk_counts(wl, q):
+    """Algorithmic bytes and flops of one multi-token launch with q new tokens
+    per sequence: every cached token's K/V read once (shared prefix pages
+    once), the queries read and the outputs written once; two products of D
+    multiply-adds per (query token, head, attended position)."""
+    esz, B, Hq, Hkv, D = wl.elem_bytes, wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    L = wl.context_lens.astype(np.int64)
+    per_token = 2 * Hkv * D * esz
+    unique_tokens = len(wl.prefill_slots) + int((wl.new_slots >= 0).sum())
+    rows = B * q * Hq * D * esz
+    tables = int(((L + 15) // 16).sum()) * 4 + B * 4 + (B + 1) * 4
+    attended = int(sum(q * int(l) - q * (q - 1) // 2 for l in L))  # positions L-q .. L-1
+    return {"kv_unique": unique_tokens * per_token, "query": rows, "out": rows, "tables": tables,
+            "kernel": unique_tokens * per_token + 2 * rows + tables,
+            "cache_write": B * q * (2 * per_token + 8),
+            "flops": 4 * D * Hq * attended}
+
+
+def run_chunk_config(cid, args):
+    import torch
+
+    import paged_kv_decode_pa_amd as pa
+    from workloads import bf16_bits_from_f32, config_by_id, make_chunk_queries, make_workload
+
+    cfg = config_by_id(cid)
+    wl = make_workload(cfg, share_prefix=not args.unshared)
+    if wl.dtype != "bf16":
+        raise SystemExit("--chunk needs a bf16 workload")
+    q = args.chunk
+    if q > int(wl.context_lens.min()):
+        raise SystemExit(f"--chunk {q} exceeds the shortest context")
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    P, Hkv, D, Hq, B = wl.page_size, wl.num_kv_heads, wl.head_dim, wl.num_q_heads, wl.num_seqs
+    k_cache = torch.full((wl.num_pages, Hkv, P, D), float("nan"), dtype=torch.bfloat16, device=dev)
+    v_cache = torch.full((wl.num_pages, Hkv, D, P), float("nan"), dtype=torch.bfloat16, device=dev)
+    pa.pa_reshape_and_cache(up(wl.prefill_key), up(wl.prefill_value), k_cache, v_cache,
+                            torch.from_numpy(wl.prefill_slots).to(dev))
+    pa.pa_reshape_and_cache(up(wl.new_key), up(wl.new_value), k_cache, v_cache,
+                            torch.from_numpy(wl.new_slots).to(dev))
+    qpay, qs = make_chunk_queries(wl, [q] * B, seed=cid)
+    query = up(qpay)
+    query_start = torch.from_numpy(qs).to(dev)
+    # The q new tokens' K/V rows (positions L-q .. L-1 of each sequence),
+    # rewritten by every step as a verification step would append them.
+    rng = np.random.default_rng(100 + cid)
+    kv_shape = (B * q, Hkv, D)
+    new_k = up(bf16_bits_from_f32(rng.standard_normal(kv_shape, dtype=np.float32)))
+    new_v = up(bf16_bits_from_f32(rng.standard_normal(kv_shape, dtype=np.float32)))
+    slots = np.empty(B * q, dtype=np.int64)
+    for b in range(B):
+        for i in range(q):
+            pos = int(wl.context_lens[b]) - q + i
+            slots[b * q + i] = int(wl.block_tables[b, pos // P]) * P + pos % P
+    slots_d = torch.from_numpy(slots).to(dev)
+    tables = torch.from_numpy(wl.block_tables).to(dev)
+    lens = torch.from_numpy(wl.context_lens).to(dev)
+    out = torch.empty_like(query)
+    flush_buf = None if args.no_flush else torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None, marks=True):
+        if ev:
+            ev[0].record()
+        pa.pa_reshape_and_cache(new_k, new_v, k_cache, v_cache, slots_d)
+        if ev and marks:
+            ev[1].record()
+        pa.pa_chunk_attention(out, query, k_cache, v_cache, tables, lens, query_start, q, wl.scale)
+        if ev:
+            ev[2].record()
+
+    def timed(marks):
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                  for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for k in range(args.steps):
+            if flush_buf is not None:
+                flush_buf.sum()
+            step(events[k], marks)
+        torch.cuda.synchronize()
+        return events
+
+    for _ in range(args.warmup):
+        if flush_buf is not None:
+            flush_buf.sum()
+        step()
+    torch.cuda.synchronize()
+    step_ev = timed(marks=False)
+    ev = timed(marks=True)
+    if not torch.isfinite(out.float()).all():
+        raise RuntimeError("non-finite chunk attention output")
+    step_ms = [e[0].elapsed_time(e[2]) for e in step_ev]
+    cache_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    attn_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    nb = chunk_counts(wl, q)
+    t_step = float(np.mean(step_ms)) * 1e-3
+    t_attn = float(np.mean(attn_ms)) * 1e-3
+    gbs = nb["kernel"] / t_attn / 1e9
+    tflops = nb["flops"] / t_attn / 1e12
+    hbm_frac, mfma_frac = gbs / PEAK_HBM_GBS, tflops / PEAK_BF16_TFLOPS
+    bound = "hbm" if hbm_frac >= mfma_frac else "mfma"
+    roof = ({"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+             "frac": round(hbm_frac, 4)} if bound == "hbm" else
+            {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+             "unit": "TFLOP/s", "frac": round(mfma_frac, 4)})
+    roof.update({"traffic": None, "kernel": f"chunk_attention_kernel<{D}>",
+                 "algorithmic_bytes_per_launch": nb["kernel"], "flops_per_launch": nb["flops"],
+                 "hbm_gbs": round(gbs, 1), "bf16_tflops": round(tflops, 2),
+                 "mean_launch_us": round(t_attn * 1e6, 2)})
+    return {
+        "metric": CHUNK_METRIC,
+        "value": round(B * q / t_step, 1),
+        "unit": "query tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[cid] + f"; {q} new tokens per sequence",
+                   "batch": B, "new_tokens_per_seq": q, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": D, "page_size": P, "prefix_pages_shared": not args.unshared,
+                   "cache_flush_between_steps": flush_buf is not None,
+                   "parallelism": "none (1 GPU)"},
+        "kernels_ms": {"cache_write": stats(cache_ms), "chunk_attention": stats(attn_ms),
+                       "step": stats(step_ms)},
+        "bytes": nb,
+        "roofline": roof,
+    }
+
+
 def cpu_baseline(wl, budget_s, nb, t_step_gpu):
     """The fp64 oracle, as it stands, on a bounded sample of the same batch:
     whole sequences in batch order until the time budget is spent."""
@@ -368,6 +507,9 @@ def main():
     import paged_kv_decode_pa_amd as pa
 
     pa.load()
+    if args.chunk:
+        print(json.dumps(run_chunk_config(args.config, args)), flush=True)
+        return
     others = [c for c in (1, 2, 3, 4, 5) if c != args.config] if args.all else []
     for cid in others:
         print(json.dumps(run_config(cid, args, headline=False)), file=sys.stderr, flush=True)

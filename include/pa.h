@@ -154,6 +154,44 @@ int pa_decode(void* out, const void* query, const void* k_cache, const void* v_c
               float* partial_sum, int dtype, void* stream);
 
 /*
+ * pa_chunk_attention — several new query tokens per sequence, causal.
+ *
+ * The step beside decode that chunked prefill and the verification of
+ * drafted tokens run (llm-d blog post, the two phases of inference and the
+ * disaggregated P/D paragraph; TensorRT Edge-LLM "HTTP Inference Server
+ * Architecture", "Model Loading": an optional draft checkpoint).  Sequence b
+ * has q_len_b = query_start[b + 1] - query_start[b] new tokens: the last
+ * q_len_b positions of its context, whose K/V are already in the pools (write
+ * them with pa_reshape_and_cache first).  Query row query_start[b] + i is
+ * the token at position p = L_b - q_len_b + i and attends to positions 0..p:
+ *     out[row][h] = sum_{t <= p} softmax_t(scale * q[row][h] . k[b][t][g]) v[b][t][g]
+ * With q_len_b = 1 for every b this is pa_decode's single-pass result.
+ *
+ *   out            [num_query_tokens][num_q_heads][head_dim], bf16; rows of
+ *                  every sequence are written.
+ *   query          [num_query_tokens][num_q_heads][head_dim], bf16.
+ *   query_start    int32 [num_seqs + 1], device: nondecreasing, query_start[0]
+ *                  = 0, query_start[num_seqs] = num_query_tokens.
+ *   max_query_len  host bound on q_len_b (sizes the grid); 0 <= q_len_b <=
+ *                  min(max_query_len, L_b) is required of the device data (a
+ *                  sequence with no new token has no rows).
+ *   the rest       as in pa_decode (pools, block tables, context lengths,
+ *                  scale, page size).
+ * Results are deterministic and do not depend on page placement.  A sequence
+ * whose q_len_b exceeds L_b gets unspecified rows, and one whose rows fall
+ * outside [0, num_query_tokens) gets none written (no fault either way).  bf16 only:
+ * PA_DTYPE_F32 returns PA_ERR_UNSUPPORTED.  max_query_len above
+ * num_query_tokens, or a NULL pointer, returns PA_ERR_INVALID_ARGUMENT;
+ * num_seqs, num_query_tokens or max_query_len of 0 is a no-op.
+ */
+int pa_chunk_attention(void* out, const void* query, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens,
+                       const int32_t* query_start, int num_seqs, int num_query_tokens,
+                       int max_query_len, int num_q_heads, int num_kv_heads, int head_dim,
+                       int page_size, int max_pages_per_seq, int64_t num_pages, float scale,
+                       int dtype, void* stream);
+
+/*
  * pa_decode_valu — pa_decode with the vector-ALU kernel forced.
  *
  * Same arguments, layouts, results contract and errors as pa_decode.  For

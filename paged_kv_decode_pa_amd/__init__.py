@@ -8,6 +8,7 @@ from ._lib import (  # noqa: F401
     PAGE_SIZE,
     PaError,
     load,
+    pa_chunk_attention,
     pa_decode,
     pa_decode_reduce,
     pa_decode_valu,

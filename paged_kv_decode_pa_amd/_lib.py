@@ -36,6 +36,9 @@ _SIGNATURES = {
     "pa_decode_valu": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32,
                        _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _i32, _c_void_p,
                        _c_void_p, _c_void_p, _i32, _c_void_p],
+    "pa_chunk_attention": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                           _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
+                           _f32, _i32, _c_void_p],
     "pa_decode_reduce": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
                          _i32, _i32, _i32, _c_void_p],
     "pa_status_string": [_i32],
@@ -159,6 +162,28 @@ def pa_decode(out, query, k_cache, v_cache, block_tables, context_lens, scale,
     partial buffers are written (then call pa_decode_reduce)."""
     _decode("pa_decode", out, query, k_cache, v_cache, block_tables, context_lens, scale,
             partition_size, partial_out, partial_max, partial_sum, stream)
+
+
+def pa_chunk_attention(out, query, k_cache, v_cache, block_tables, context_lens, query_start,
+                       max_query_len, scale, stream=None) -> None:
+    """Causal attention of several new tokens per sequence; see include/pa.h.
+    query/out [T][Hq][D] bf16; query_start int32 [B + 1]; max_query_len is a
+    host bound on every sequence's new-token count."""
+    T, Hq, D = query.shape
+    B = context_lens.shape[0]
+    Hkv = k_cache.shape[1]
+    if k_cache.shape[2:] != (PAGE_SIZE, D) or v_cache.shape[1:] != (Hkv, D, PAGE_SIZE):
+        raise ValueError("pool shape does not match query")
+    if block_tables.shape[0] != B or tuple(query_start.shape) != (B + 1,):
+        raise ValueError("block_tables / query_start do not match the batch")
+    if out.shape != query.shape or out.dtype != query.dtype:
+        raise ValueError("out must match query")
+    lib = load()
+    _check("pa_chunk_attention", lib.pa_chunk_attention(
+        _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        _ptr(context_lens), _ptr(query_start), B, T, int(max_query_len), Hq, Hkv, D, PAGE_SIZE,
+        block_tables.shape[1], k_cache.shape[0], float(scale), _dtype_code(query),
+        _stream(stream)))
 
 
 def pa_decode_valu(out, query, k_cache, v_cache, block_tables, context_lens, scale,

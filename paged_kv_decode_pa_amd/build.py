@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpa.so")
 SOURCES = ["pa_api.hip", "reshape_and_cache.hip", "decode_mfma.hip", "decode_valu.hip",
-           "decode_reduce.hip"]
+           "decode_reduce.hip", "chunk_mfma.hip"]
 ARCH = "gfx950"
 
 
@@ -37,6 +37,14 @@ def command(out: str = LIB) -> list:
         *[os.path.join(CSRC, s) for s in SOURCES],
         "-o", out,
     ]
+
+
+def device_asm_command(source: str, out: str) -> list:
+    """hipcc line that writes the gfx950 assembly of one source, compiled with
+    the same flags as the library."""
+    lib = command(out)
+    flags = [c for c in lib if not c.endswith(".hip") and c not in ("-shared", "-fPIC")]
+    return [*flags, "--cuda-device-only", "-S", os.path.join(CSRC, source)]
 
 
 def build(verbose: bool = False) -> str:

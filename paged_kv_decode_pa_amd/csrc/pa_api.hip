@@ -14,6 +14,7 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
                                     void* v_cache, const int64_t* slots, int64_t num_tokens,
                                     int num_kv_heads, int head_dim, int64_t num_pages, bool bf16,
                                     hipStream_t stream);
+hipError_t launch_chunk_attention(const ChunkParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_reduce(void* out, const float* part_out, const float* part_max,
                                 const float* part_sum, const int32_t* context_lens, int num_seqs,
                                 int num_q_heads, int head_dim, int partition_size, int max_parts,
@@ -124,6 +125,53 @@ int pa_decode(void* out, const void* query, const void* k_cache, const void* v_c
                      context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
                      max_pages_per_seq, num_pages, scale, partition_size, max_num_partitions,
                      partial_out, partial_max, partial_sum, dtype, stream);
+}
+
+int pa_chunk_attention(void* out, const void* query, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens,
+                       const int32_t* query_start, int num_seqs, int num_query_tokens,
+                       int max_query_len, int num_q_heads, int num_kv_heads, int head_dim,
+                       int page_size, int max_pages_per_seq, int64_t num_pages, float scale,
+                       int dtype, void* stream) {
+  if (num_seqs < 0 || num_query_tokens < 0 || max_query_len < 0 || num_q_heads <= 0 ||
+      num_kv_heads <= 0 || max_pages_per_seq <= 0 || num_pages <= 0)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (int s = check_common(head_dim, page_size, dtype)) return s;
+  if (dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;  // matrix-core kernel only
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARGUMENT;
+  const int group = num_q_heads / num_kv_heads;
+  if (group > PA_MAX_GQA_GROUP) return PA_ERR_UNSUPPORTED;
+  if (!out || !query || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(query) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_ERR_INVALID_ARGUMENT;
+  if (!isfinite(scale)) return PA_ERR_INVALID_ARGUMENT;
+  if (max_query_len > num_query_tokens) return PA_ERR_INVALID_ARGUMENT;
+  const int64_t blocks = (int64_t(max_query_len) * group + 15) / 16;
+  const int64_t units = int64_t(num_seqs) * num_kv_heads * blocks;
+  if (units > INT_MAX / 2) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0) return PA_OK;
+
+  pa::ChunkParams p;
+  p.out = out;
+  p.query = query;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.query_start = query_start;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = group;
+  p.max_pages_per_seq = max_pages_per_seq;
+  p.num_pages = num_pages;
+  p.scale_log2 = scale * pa::kLog2e;
+  p.num_query_tokens = num_query_tokens;
+  p.blocks_per_seq = int(blocks);
+  p.num_units = int(units);
+  const hipError_t err = pa::launch_chunk_attention(p, head_dim, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 int pa_decode_valu(void* out, const void* query, const void* k_cache, const void* v_cache,

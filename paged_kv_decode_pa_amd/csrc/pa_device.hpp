@@ -36,6 +36,31 @@ struct DecodeParams {
   int num_units;            // num_seqs * num_partitions * num_kv_heads
 };
 
+// Multi-token causal attention over the same cache: sequence b's new query
+// tokens are rows query_start[b] .. query_start[b + 1] - 1 of `query`, at
+// positions L_b - q_len_b + i.  A work unit is (sequence, kv head, column
+// block): the block's 16 matrix columns are (query token, head of the group)
+// pairs, column c = i * group + h.
+struct ChunkParams {
+  void* out;
+  const void* query;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start;
+  int num_seqs;
+  int num_q_heads;
+  int num_kv_heads;
+  int group;
+  int max_pages_per_seq;
+  int64_t num_pages;
+  float scale_log2;
+  int num_query_tokens;
+  int blocks_per_seq;  // ceil(max_query_len * group / 16)
+  int num_units;       // num_seqs * num_kv_heads * blocks_per_seq
+};
+
 // Number of workgroups: one per work unit.
 __host__ __device__ inline int decode_grid(int num_units) { return num_units; }
 

@@ -101,6 +101,44 @@ def test_decode_empty_batch_is_a_noop():
                                            partial_sum=P)) == OK
 
 
+def chunk_args(**kw):
+    a = dict(out=P, query=P, k_cache=P, v_cache=P, block_tables=P, context_lens=P,
+             query_start=P, num_seqs=4, num_query_tokens=16, max_query_len=4, num_q_heads=32,
+             num_kv_heads=8, head_dim=128, page_size=16, max_pages_per_seq=8, num_pages=64,
+             scale=0.088, dtype=BF16, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+CHUNK_CASES = [
+    ("null_out", dict(out=None), INVAL),
+    ("null_query_start", dict(query_start=None), INVAL),
+    ("null_tables", dict(block_tables=None), INVAL),
+    ("f32", dict(dtype=F32), UNSUP),
+    ("head_dim_96", dict(head_dim=96), UNSUP),
+    ("page_size_8", dict(page_size=8), UNSUP),
+    ("group_above_16", dict(num_q_heads=32, num_kv_heads=1), UNSUP),
+    ("heads_not_divisible", dict(num_q_heads=30), INVAL),
+    ("max_len_above_tokens", dict(max_query_len=17), INVAL),
+    ("negative_tokens", dict(num_query_tokens=-1), INVAL),
+    ("negative_max_len", dict(max_query_len=-1), INVAL),
+    ("misaligned_query", dict(query=P + 2), INVAL),
+    ("nan_scale", dict(scale=float("nan")), INVAL),
+    ("zero_pool", dict(num_pages=0), INVAL),
+]
+
+
+@pytest.mark.parametrize("name,kw,want", CHUNK_CASES, ids=[c[0] for c in CHUNK_CASES])
+def test_chunk_attention_rejects(name, kw, want):
+    assert pa.load().pa_chunk_attention(*chunk_args(**kw)) == want
+
+
+def test_chunk_attention_empty_is_a_noop():
+    lib = pa.load()
+    assert lib.pa_chunk_attention(*chunk_args(num_seqs=0)) == OK
+    assert lib.pa_chunk_attention(*chunk_args(num_query_tokens=0, max_query_len=0)) == OK
+
+
 def cache_args(**kw):
     a = dict(key=P, value=P, k_cache=P, v_cache=P, slot_mapping=P, num_tokens=8, num_kv_heads=8,
              head_dim=128, page_size=16, num_pages=64, dtype=BF16, stream=None)

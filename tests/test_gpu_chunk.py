@@ -1,0 +1,111 @@
+"""pa_chunk_attention (several new tokens per sequence, causal) against the
+fp64 oracle, plus the structural properties the bf16 tolerance could hide:
+one token per sequence reproduces pa_decode bit for bit, later tokens' K/V
+never touch earlier rows, and page placement changes nothing."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_decode_pa_amd as pa
+from tests.gpu_helpers import (DEV, TOL, DeviceWorkload, bits_of, config_device, config_workload,
+                               f64_of, max_err, say, to_dev)
+from tests.oracle_pins import fill_pools
+from workloads import make_chunk_queries, make_custom_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def run_chunk(dev, query, query_start, max_q=None):
+    wl = dev.wl
+    q = to_dev(query, wl.dtype)
+    qs = torch.from_numpy(np.asarray(query_start, dtype=np.int32)).to(DEV)
+    out = torch.full_like(q, float("nan"))
+    lens = np.diff(np.asarray(query_start))
+    mq = int(lens.max()) if max_q is None else max_q
+    pa.pa_chunk_attention(out, q, dev.k_cache, dev.v_cache, dev.block_tables, dev.context_lens,
+                          qs, mq, wl.scale)
+    torch.cuda.synchronize()
+    return out
+
+
+def chunk_reference(wl, query, query_start):
+    k, v = fill_pools(oracle, wl)
+    return oracle.chunk_attention(query, k, v, wl.block_tables, wl.context_lens, query_start,
+                                  wl.scale, wl.page_size, wl.dtype)
+
+
+@pytest.mark.parametrize("cid", [2, 5, 3])
+def test_one_token_per_sequence_is_decode(cid):
+    say(f"[chunk] q_len = 1 equals single-pass decode, config {cid}")
+    dev = config_device(cid)
+    wl = dev.wl
+    qs = np.arange(wl.num_seqs + 1, dtype=np.int32)
+    got = run_chunk(dev, wl.query, qs)
+    assert np.array_equal(bits_of(got), bits_of(dev.decode(0)))
+
+
+CASES = [
+    # lengths, new-token counts, Hq, Hkv, D
+    ([300, 77, 129, 16], [64, 77, 5, 1], 8, 2, 128),     # whole-sequence prefill, group 4
+    ([1000, 33, 512], [7, 2, 16], 32, 8, 128),           # drafted tokens, group 4
+    ([700, 48], [33, 17], 16, 1, 128),                   # group 16: one token per block
+    ([257, 90], [40, 90], 8, 8, 64),                     # no grouping: 16 tokens per block
+    ([130, 64, 200], [12, 3, 0], 12, 4, 64),             # group 3 straddles blocks; q_len 0
+    ([2048 + 300], [300], 8, 1, 128),                    # chunked prefill on a long context
+]
+
+
+@pytest.mark.parametrize("lens,q_lens,Hq,Hkv,D", CASES)
+def test_chunk_matches_oracle(lens, q_lens, Hq, Hkv, D):
+    say(f"[chunk] {lens} q {q_lens} {Hq}/{Hkv}/{D}")
+    wl = make_custom_workload(lens, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                              seed=sum(lens) + Hq)
+    query, qs = make_chunk_queries(wl, q_lens, seed=len(lens) + D)
+    ref = chunk_reference(wl, query, qs)
+    dev = DeviceWorkload(wl)
+    got = run_chunk(dev, query, qs)
+    err = max_err(got, ref)
+    say(f"    max abs err {err:.3e}")
+    assert err <= TOL["bf16"]
+    # a looser grid bound only adds units that exit at once
+    assert np.array_equal(bits_of(run_chunk(dev, query, qs, max_q=int(qs[-1]))), bits_of(got))
+
+
+def test_spec_decode_batch_at_config_2_shape():
+    """Four new tokens for each of config 2's 64 sequences (the shape of a
+    draft verification step), against the oracle."""
+    say("[chunk] config 2 shape, 4 new tokens per sequence")
+    wl = config_workload(2)
+    query, qs = make_chunk_queries(wl, [4] * wl.num_seqs, seed=2)
+    ref = chunk_reference(wl, query, qs)
+    got = run_chunk(config_device(2), query, qs)
+    assert max_err(got, ref) <= TOL["bf16"]
+
+
+def test_later_tokens_never_reach_earlier_rows():
+    say("[chunk] causality on the GPU")
+    wl = make_custom_workload([200], num_q_heads=8, num_kv_heads=2, head_dim=128, seed=5)
+    query, qs = make_chunk_queries(wl, [40], seed=6)               # positions 160..199
+    dev = DeviceWorkload(wl)
+    base = bits_of(run_chunk(dev, query, qs))
+    p = 181                                                          # row p - 160 = 21
+    page, slot = int(wl.block_tables[0, p // 16]), p % 16
+    dev.k_cache[page, :, slot, :] *= -3
+    dev.v_cache[page, :, :, slot] += 1
+    moved = bits_of(run_chunk(dev, query, qs))
+    assert np.array_equal(moved[:21], base[:21])
+    assert not np.array_equal(moved[21], base[21])
+
+
+def test_placement_and_repeats_do_not_change_bits():
+    say("[chunk] placement invariance and determinism")
+    lens, q_lens = [513, 40, 1000], [9, 40, 3]
+    a = make_custom_workload(lens, num_q_heads=32, num_kv_heads=8, head_dim=128, seed=9)
+    b = make_custom_workload(lens, num_q_heads=32, num_kv_heads=8, head_dim=128, seed=9,
+                             placement_seed=3)
+    query, qs = make_chunk_queries(a, q_lens, seed=10)
+    ga = bits_of(run_chunk(DeviceWorkload(a), query, qs))
+    db = DeviceWorkload(b)
+    assert np.array_equal(ga, bits_of(run_chunk(db, query, qs)))
+    assert np.array_equal(ga, bits_of(run_chunk(db, query, qs)))
