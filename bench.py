@@ -36,6 +36,9 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["paged_kv_decode_pa_amd/csrc/decode_mfma.hip",
                   "paged_kv_decode_pa_amd/csrc/page_stream.hpp",
                   "paged_kv_decode_pa_amd/csrc/pa_device.hpp"]
+CHUNK_KERNEL_SOURCES = ["paged_kv_decode_pa_amd/csrc/chunk_mfma.hip",
+                        "paged_kv_decode_pa_amd/csrc/page_stream.hpp",
+                        "paged_kv_decode_pa_amd/csrc/pa_device.hpp"]
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 CHUNK_METRIC = ("multi-token causal attention over the paged cache (draft verification / "
                 "chunked prefill): query tokens/s, 1 GPU")
@@ -107,18 +110,18 @@ def byte_counts(wl, partition_size):
             "step": decode + reduce + cache_write}
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=KERNEL_SOURCES):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(cid, partition_size):
-    """HBM bytes per decode launch from a committed counter summary, or None
-    when the summary is absent or the kernel changed since it was taken."""
-    path = os.path.join(PROFILES, f"traffic_decode_mfma_cfg{cid}.txt")
+def read_profile_kv(name, sources):
+    """key: value lines of a committed counter summary, or None when it is
+    absent or the kernel's sources changed since the counters were taken."""
+    path = os.path.join(PROFILES, name)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -127,14 +130,32 @@ def read_traffic(cid, partition_size):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash(sources):
         return None
-    if int(kv.get("partition_size", -1)) != partition_size:
+    return kv
+
+
+def read_traffic(cid, partition_size):
+    """HBM bytes per decode launch from a committed counter summary, or None
+    when the summary is absent or the kernel changed since it was taken."""
+    kv = read_profile_kv(f"traffic_decode_mfma_cfg{cid}.txt", KERNEL_SOURCES)
+    if kv is None or int(kv.get("partition_size", -1)) != partition_size:
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def copy_calibration(dev):
+    """Three 512 MiB device copies: the known sizes that scale the HBM counters."""
+    import torch
+
+    src = torch.empty(1 << 27, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
 
 
 def run_config(cid, args, headline):
@@ -264,11 +285,7 @@ def run_config(cid, args, headline):
         del graph
 
     if args.copy_calibration:
-        src = torch.empty(1 << 27, dtype=torch.float32, device=dev).fill_(1.0)  # 512 MiB
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
+        copy_calibration(dev)
 
     nb = byte_counts(wl, ps)
     t_step = float(np.mean(step_ms)) * 1e-3
@@ -418,6 +435,8 @@ def run_chunk_config(cid, args):
     ev = timed(marks=True)
     if not torch.isfinite(out.float()).all():
         raise RuntimeError("non-finite chunk attention output")
+    if args.copy_calibration:
+        copy_calibration(dev)
     step_ms = [e[0].elapsed_time(e[2]) for e in step_ev]
     cache_ms = [e[0].elapsed_time(e[1]) for e in ev]
     attn_ms = [e[1].elapsed_time(e[2]) for e in ev]
@@ -432,7 +451,14 @@ def run_chunk_config(cid, args):
              "frac": round(hbm_frac, 4)} if bound == "hbm" else
             {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
              "unit": "TFLOP/s", "frac": round(mfma_frac, 4)})
-    roof.update({"traffic": None, "kernel": f"chunk_attention_kernel<{D}>",
+    kv = read_profile_kv(f"traffic_chunk_attention_cfg{cid}_q{q}.txt", CHUNK_KERNEL_SOURCES)
+    traffic = None
+    if kv is not None and not args.unshared:
+        try:
+            traffic = float(kv["hbm_bytes_per_launch"])
+        except (KeyError, ValueError):
+            traffic = None
+    roof.update({"traffic": traffic, "kernel": f"chunk_attention_kernel<{D}>",
                  "algorithmic_bytes_per_launch": nb["kernel"], "flops_per_launch": nb["flops"],
                  "hbm_gbs": round(gbs, 1), "bf16_tflops": round(tflops, 2),
                  "mean_launch_us": round(t_attn * 1e6, 2)})
