@@ -8,14 +8,16 @@
 // matrix tile generalised from "the group's query heads" to (query token,
 // head) pairs: column c = i * group + h of a block is token i, head h.  So a
 // group of 4 puts four consecutive tokens of one kv head's four query heads
-// in one tile, and every K/V page loaded serves all of them.  Scores past a
-// column's own position are masked to -inf by select, per lane.
+// in one tile.  Scores past a column's own position are masked to -inf by
+// select, per lane.
 //
-// Unit = (sequence, kv head, column block), four waves; wave w takes pages
-// w, w+4, ... up to the block's last position, and the four online-softmax
-// states merge through LDS in a fixed order.  Pages are read with cached
-// loads: the column blocks of one (sequence, kv head) reread the same pages,
-// and the kv-head-fastest unit order puts them on one XCD's L2.
+// A wave carries NB <= 4 consecutive column blocks, so every K/V tile it
+// loads serves up to 64 columns (16 new tokens at a group of 4) from one
+// read.  Unit = (sequence, kv head, group of NB blocks), four waves; wave w
+// takes pages w, w+4, ... up to the group's last position, and the four
+// online-softmax states of each block merge through LDS in a fixed order.
+// Pages are read with cached loads: a long chunk's block groups reread the
+// same pages, and the kv-head-fastest unit order puts them on one XCD's L2.
 #include "page_stream.hpp"
 
 namespace pa {
@@ -51,38 +53,25 @@ struct ColumnAttn {
     for (int db = 0; db <= D / 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Page starting at token `base`, with `valid` tokens of the context in it.
-  // A column may have no unmasked token on a page (its position precedes the
-  // page): its P is then 0, and while its reference is still -inf nothing is
-  // rescaled, so no 0 * inf or inf - inf arises.
-  //
-  // Between the score products and the first vector instruction that reads
-  // them there is no branch: with a data-dependent branch in between (the
-  // zeroing of a partial page's V, which used to sit there), the compiler let
-  // a taken branch reach the reads fewer wait states after the matrix
-  // instruction than its result needs, and the scores of whole pages came out
-  // wrong and varied from run to run.  Only the sequence's last page can hold
-  // unwritten slots, and a wave meets it only after the steady-state loop
-  // (`Tail`); there the V zeroing is done by select, with no branch at all.
-  template <bool Tail>
-  __device__ void page(PageTile<D>& t, int base, int valid) {
+  // Scores of the page starting at token `base`, base 2, with the causal
+  // mask (which also masks positions past the context).
+  __device__ void scores(const PageTile<D>& t, int base, float (&s2)[4]) const {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < D / 32; ++kb)
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[kb], qop[kb], s, 0, 0, 0);
-    float s2[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)  // causal, which also masks past the context
+    for (int e = 0; e < 4; ++e)
       s2[e] = base + 4 * j + e > pos ? -INFINITY : s[e] * scale_log2;
-    if constexpr (Tail) {
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)  // unwritten slots may hold NaN
-          t.v[db][e] = 4 * j + e < valid ? t.v[db][e] : short(0);
-    }
-    const float lm = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
-    if (__ballot(lm > m_run + kSlack) != 0) {
+  }
+
+  // Online-softmax update with the page's scores, given whether any lane's
+  // score exceeds its reference by more than kSlack (`raise`, a wave ballot).
+  // A column may have no unmasked token on a page (its position precedes the
+  // page): its P is then 0, and while its reference is still -inf the
+  // rescale factor is 0, so no 0 * inf or inf - inf arises.
+  __device__ void accumulate(const PageTile<D>& t, const float (&s2)[4], float lm, bool raise) {
+    if (raise) {
       float pm = fmaxf(lm, __shfl_xor(lm, 16));
       pm = fmaxf(pm, __shfl_xor(pm, 32));
       const float m_new = fmaxf(m_run, pm);
@@ -102,34 +91,78 @@ struct ColumnAttn {
       acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[db], pb, acc[db], 0, 0, 0);
     acc[D / 16] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pb, acc[D / 16], 0, 0, 0);
   }
+};
 
-  // Two tiles in ping-pong, as in the decode kernel; ordinal k is page
-  // page0 + step * k.  The loop stops three ordinals before the end, so the
-  // pages it computes are all full; the last one to three go through the
-  // tail step.
-  __device__ void run(PageStream<D>& ps, int page0, int L, int lane) {
-    const int n = ps.count;
-    if (n <= 0) return;
-    auto base = [&](int k) { return (page0 + ps.step * k) * kPage; };
-    PageTile<D> ta, tb;
-    bool ok_a = ps.template issue<false>(ta, 0, lane);
-    bool ok_b = ps.template issue<false>(tb, 1, lane);
-    int k = 0;
-    for (; k + 3 < n; k += 2) {
-      if (ok_a) page<false>(ta, base(k), kPage);
-      ok_a = ps.template issue<false>(ta, k + 2, lane);
-      if (ok_b) page<false>(tb, base(k + 1), kPage);
-      ok_b = ps.template issue<false>(tb, k + 3, lane);
+// Slots at or past `valid` of a partial page may hold NaN; 0 * NaN would
+// reach the accumulator, so their V elements are zeroed (by select).
+template <int D>
+__device__ inline void zero_past(PageTile<D>& t, int valid, int j) {
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t.v[db][e] = 4 * j + e < valid ? t.v[db][e] : short(0);
+}
+
+// One page for the wave's NB column blocks.  All blocks' score products and
+// their first vector reads come before the first branch (the ballots'
+// rescales): with a data-dependent branch between a matrix instruction and
+// the reads of its result, the compiler was seen to let a taken branch reach
+// the reads fewer wait states after the instruction than the result needs
+// (wrong, run-to-run varying scores).
+template <int D, int NB>
+__device__ inline void page_blocks(ColumnAttn<D> (&wa)[NB], const PageTile<D>& t, int base) {
+  float s2[NB][4];
+  float lm[NB];
+  bool raise[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) wa[nb].scores(t, base, s2[nb]);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    lm[nb] = fmaxf(fmaxf(s2[nb][0], s2[nb][1]), fmaxf(s2[nb][2], s2[nb][3]));
+    raise[nb] = __ballot(lm[nb] > wa[nb].m_run + kSlack) != 0;
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) wa[nb].accumulate(t, s2[nb], lm[nb], raise[nb]);
+}
+
+// Two tiles in ping-pong, as in the decode kernel; ordinal k is page
+// page0 + step * k.  The loop stops three ordinals before the end, so the
+// pages it computes are all full (only the sequence's last page can be
+// partial); the last one to three are zeroed past the context first.
+template <int D, int NB>
+__device__ inline void run_blocks(ColumnAttn<D> (&wa)[NB], PageStream<D>& ps, int page0, int L,
+                                  int lane) {
+  const int n = ps.count;
+  if (n <= 0) return;
+  const int j = lane >> 4;
+  auto base = [&](int k) { return (page0 + ps.step * k) * kPage; };
+  PageTile<D> ta, tb;
+  bool ok_a = ps.template issue<false>(ta, 0, lane);
+  bool ok_b = ps.template issue<false>(tb, 1, lane);
+  int k = 0;
+  for (; k + 3 < n; k += 2) {
+    if (ok_a) page_blocks<D, NB>(wa, ta, base(k));
+    ok_a = ps.template issue<false>(ta, k + 2, lane);
+    if (ok_b) page_blocks<D, NB>(wa, tb, base(k + 1));
+    ok_b = ps.template issue<false>(tb, k + 3, lane);
+  }
+  const int rem = n - k;
+  if (ok_a) {
+    zero_past(ta, L - base(k), j);
+    page_blocks<D, NB>(wa, ta, base(k));
+  }
+  if (rem >= 2) {
+    const bool ok_c = rem == 3 && ps.template issue<false>(ta, k + 2, lane);
+    if (ok_b) {
+      zero_past(tb, L - base(k + 1), j);
+      page_blocks<D, NB>(wa, tb, base(k + 1));
     }
-    const int rem = n - k;
-    if (ok_a) page<true>(ta, base(k), L - base(k));
-    if (rem >= 2) {
-      const bool ok_c = rem == 3 && ps.template issue<false>(ta, k + 2, lane);
-      if (ok_b) page<true>(tb, base(k + 1), L - base(k + 1));
-      if (ok_c) page<true>(ta, base(k + 2), L - base(k + 2));
+    if (ok_c) {
+      zero_past(ta, L - base(k + 2), j);
+      page_blocks<D, NB>(wa, ta, base(k + 2));
     }
   }
-};
+}
 
 // LDS of the four-wave merge: per wave a reference and a sum per column and
 // the un-normalised accumulator [wave][column][D].
@@ -137,15 +170,15 @@ __host__ __device__ inline size_t chunk_lds_bytes(int head_dim) {
   return sizeof(float) * (2 * kWaves * 16 + size_t(kWaves) * 16 * head_dim);
 }
 
-template <int D>
+template <int D, int NB>
 __global__ __launch_bounds__(kBlock) void chunk_attention_kernel(ChunkParams p) {
   extern __shared__ float smem[];
   const int u = blockIdx.x;
   if (u >= p.num_units) return;
   const int kvh = u % p.num_kv_heads;
   const int rest = u / p.num_kv_heads;
-  const int cb = rest % p.blocks_per_seq;
-  const int seq = rest / p.blocks_per_seq;
+  const int grp = rest % p.groups_per_seq;
+  const int seq = rest / p.groups_per_seq;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, j = lane >> 4;
@@ -154,17 +187,11 @@ __global__ __launch_bounds__(kBlock) void chunk_attention_kernel(ChunkParams p) 
   const int q0 = p.query_start[seq];
   const int q_len = p.query_start[seq + 1] - q0;
   const int cols = q_len * G;                  // (token, head) columns of this kv head
-  const int c_lo = cb * 16;
+  const int c0 = grp * NB * 16;                // first column of the group's first block
   // The whole workgroup leaves together; malformed offsets write nothing.
-  if (q_len <= 0 || c_lo >= cols || q0 < 0 || q0 + q_len > p.num_query_tokens) return;
+  if (q_len <= 0 || c0 >= cols || q0 < 0 || q0 + q_len > p.num_query_tokens) return;
   const int L = min(p.context_lens[seq], p.max_pages_per_seq * kPage);
-
-  const int c = c_lo + r;
-  const bool real = c < cols;
-  const int i = real ? c / G : 0;
-  const int h = real ? c % G : 0;
-  const int pos = L - q_len + i;               // < 0 only if q_len exceeds the context
-  const int last_pos = L - q_len + (min(c_lo + 15, cols - 1) / G);
+  const int last_pos = L - q_len + (min(c0 + NB * 16 - 1, cols - 1) / G);
   const int n_pages = last_pos >= 0 ? last_pos / kPage + 1 : 0;
 
   PageStream<D> ps;
@@ -182,45 +209,72 @@ __global__ __launch_bounds__(kBlock) void chunk_attention_kernel(ChunkParams p) 
   ps.start(lane);
   ps.count = w < n_pages ? (n_pages - w + kWaves - 1) / kWaves : 0;
 
-  ColumnAttn<D> wa;
-  const uint16_t* qrow =
-      static_cast<const uint16_t*>(p.query) + (size_t(q0 + i) * p.num_q_heads + kvh * G + h) * D;
-  wa.init(qrow, real, r, j, real ? pos : -1, p.scale_log2);
-  wa.run(ps, w, L, lane);
+  ColumnAttn<D> wa[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int c = c0 + 16 * nb + r;
+    const bool real = c < cols;
+    const int i = real ? c / G : 0;
+    const int h = real ? c % G : 0;
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.query) +
+                           (size_t(q0 + i) * p.num_q_heads + kvh * G + h) * D;
+    // position of the column's token (< 0 only if q_len exceeds the context)
+    wa[nb].init(qrow, real, r, j, real ? L - q_len + i : -1, p.scale_log2);
+  }
+  run_blocks<D, NB>(wa, ps, w, L, lane);
 
-  // Merge the four waves per column (fixed wave order) and store the rows.
+  // Merge the four waves per column (fixed wave order) and store the rows,
+  // one block at a time through the same LDS.
   float* lm = smem;                       // [kWaves][16]
   float* ll = smem + kWaves * 16;         // [kWaves][16]
   float* la = smem + 2 * kWaves * 16;     // [kWaves][16][D]
-  if (j == 0) {
-    lm[w * 16 + r] = wa.m_run;
-    ll[w * 16 + r] = wa.acc[D / 16][0];
-  }
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) la[(w * 16 + r) * D + 16 * db + 4 * j + e] = wa.acc[db][e];
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < 16 * D; idx += kBlock) {
-    const int col = idx / D;
-    const int d = idx % D;
-    const int cc = c_lo + col;
-    if (cc >= cols) continue;
-    float M = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, lm[v * 16 + col]);
-    float wsum = 0.f, num = 0.f;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
-      const float mv = lm[v * 16 + col];
-      const float f = mv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv - M);
-      wsum += ll[v * 16 + col] * f;
-      num += la[(v * 16 + col) * D + d] * f;
+  for (int nb = 0; nb < NB; ++nb) {
+    const int c_lo = c0 + 16 * nb;
+    if (c_lo >= cols) break;  // uniform: the group's remaining blocks are empty
+    if (nb > 0) __syncthreads();  // the previous block's reads are done
+    if (j == 0) {
+      lm[w * 16 + r] = wa[nb].m_run;
+      ll[w * 16 + r] = wa[nb].acc[D / 16][0];
     }
-    const int row = q0 + cc / G;
-    const int head = kvh * G + cc % G;
-    Elem<uint16_t>::store(p.out, (size_t(row) * p.num_q_heads + head) * D + d,
-                          wsum > 0.f ? num / wsum : 0.f);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        la[(w * 16 + r) * D + 16 * db + 4 * j + e] = wa[nb].acc[db][e];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 16 * D; idx += kBlock) {
+      const int col = idx / D;
+      const int d = idx % D;
+      const int cc = c_lo + col;
+      if (cc >= cols) continue;
+      float M = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) M = fmaxf(M, lm[v * 16 + col]);
+      float wsum = 0.f, num = 0.f;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) {
+        const float mv = lm[v * 16 + col];
+        const float f = mv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv - M);
+        wsum += ll[v * 16 + col] * f;
+        num += la[(v * 16 + col) * D + d] * f;
+      }
+      const int row = q0 + cc / G;
+      const int head = kvh * G + cc % G;
+      Elem<uint16_t>::store(p.out, (size_t(row) * p.num_q_heads + head) * D + d,
+                            wsum > 0.f ? num / wsum : 0.f);
+    }
+  }
+}
+
+template <int D>
+void launch_d(const ChunkParams& p, size_t lds, hipStream_t stream) {
+  const dim3 grid(p.num_units);
+  switch (p.blocks_per_wave) {
+    case 1: chunk_attention_kernel<D, 1><<<grid, kBlock, lds, stream>>>(p); break;
+    case 2: chunk_attention_kernel<D, 2><<<grid, kBlock, lds, stream>>>(p); break;
+    case 3: chunk_attention_kernel<D, 3><<<grid, kBlock, lds, stream>>>(p); break;
+    default: chunk_attention_kernel<D, 4><<<grid, kBlock, lds, stream>>>(p); break;
   }
 }
 
@@ -229,9 +283,9 @@ __global__ __launch_bounds__(kBlock) void chunk_attention_kernel(ChunkParams p) 
 hipError_t launch_chunk_attention(const ChunkParams& p, int head_dim, hipStream_t stream) {
   const size_t lds = chunk_lds_bytes(head_dim);
   if (head_dim == 128)
-    chunk_attention_kernel<128><<<dim3(p.num_units), kBlock, lds, stream>>>(p);
+    launch_d<128>(p, lds, stream);
   else
-    chunk_attention_kernel<64><<<dim3(p.num_units), kBlock, lds, stream>>>(p);
+    launch_d<64>(p, lds, stream);
   return hipGetLastError();
 }
 

@@ -148,7 +148,9 @@ int pa_chunk_attention(void* out, const void* query, const void* k_cache, const 
   if (!isfinite(scale)) return PA_ERR_INVALID_ARGUMENT;
   if (max_query_len > num_query_tokens) return PA_ERR_INVALID_ARGUMENT;
   const int64_t blocks = (int64_t(max_query_len) * group + 15) / 16;
-  const int64_t units = int64_t(num_seqs) * num_kv_heads * blocks;
+  const int64_t per_wave = blocks < 4 ? (blocks > 0 ? blocks : 1) : 4;
+  const int64_t groups = (blocks + per_wave - 1) / per_wave;
+  const int64_t units = int64_t(num_seqs) * num_kv_heads * groups;
   if (units > INT_MAX / 2) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0) return PA_OK;
 
@@ -168,7 +170,8 @@ int pa_chunk_attention(void* out, const void* query, const void* k_cache, const 
   p.num_pages = num_pages;
   p.scale_log2 = scale * pa::kLog2e;
   p.num_query_tokens = num_query_tokens;
-  p.blocks_per_seq = int(blocks);
+  p.blocks_per_wave = int(per_wave);
+  p.groups_per_seq = int(groups);
   p.num_units = int(units);
   const hipError_t err = pa::launch_chunk_attention(p, head_dim, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? PA_OK : PA_ERR_LAUNCH;

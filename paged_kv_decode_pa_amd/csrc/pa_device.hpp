@@ -38,9 +38,9 @@ struct DecodeParams {
 
 // Multi-token causal attention over the same cache: sequence b's new query
 // tokens are rows query_start[b] .. query_start[b + 1] - 1 of `query`, at
-// positions L_b - q_len_b + i.  A work unit is (sequence, kv head, column
-// block): the block's 16 matrix columns are (query token, head of the group)
-// pairs, column c = i * group + h.
+// positions L_b - q_len_b + i.  A work unit is (sequence, kv head, group of
+// up to four column blocks): a block's 16 matrix columns are (query token,
+// head of the group) pairs, column c = i * group + h.
 struct ChunkParams {
   void* out;
   const void* query;
@@ -57,8 +57,9 @@ struct ChunkParams {
   int64_t num_pages;
   float scale_log2;
   int num_query_tokens;
-  int blocks_per_seq;  // ceil(max_query_len * group / 16)
-  int num_units;       // num_seqs * num_kv_heads * blocks_per_seq
+  int blocks_per_wave;  // column blocks a wave carries: min(4, ceil(max_query_len * group / 16))
+  int groups_per_seq;   // ceil(ceil(max_query_len * group / 16) / blocks_per_wave)
+  int num_units;        // num_seqs * num_kv_heads * groups_per_seq
 };
 
 // Number of workgroups: one per work unit.
