@@ -1,5 +1,6 @@
 """Plain fp64 CPU oracle for paged-KV decode attention (and multi-token
-causal queries over the same cache).
+causal queries over the same cache, and the page export/import of a KV
+hand-off).
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
 link this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
@@ -20,7 +21,9 @@ from .paged_attention import (  # noqa: F401
     combine_partitions,
     decode,
     decode_partials,
+    export_pages,
     gather_sequence,
+    import_pages,
     partition_attention,
     to_float64,
 )

@@ -255,3 +255,53 @@ def chunk_attention(query, k_cache, v_cache, block_tables, context_lens, query_s
         out[lo:hi] = causal_attention(q64[lo:hi], to_float64(K, dtype), to_float64(V, dtype),
                                       scale, positions)
     return out
+
+# ---------------------------------------------------------------- page hand-off
+# The llm-d router blog post (disaggregated prefill/decode section) describes
+# the KV cache computed on prefill pods being transferred to decode pods.  The
+# part of that hand-off that runs on a GPU is a gather of a sequence's pages
+# into one buffer on the sending side and a scatter of that buffer into pages
+# of the receiving pool.  Buffer layout read here:
+#
+#     buffer[0][i] = k_cache[page_ids[i]]   flattened ([Hkv][page_size][D])
+#     buffer[1][i] = v_cache[page_ids[i]]   flattened ([Hkv][D][page_size])
+#
+# Page ids outside [0, num_pages) are skipped: export leaves their buffer
+# blocks as they were, import writes nothing for them.  Both directions are
+# pure data movement; the bits are the input bits.
+
+
+def export_pages(k_cache, v_cache, page_ids, buffer=None):
+    """Gather the listed pages into a new buffer [2][n][block] (a copy of
+    ``buffer`` when one is given, so skipped ids keep its contents)."""
+    kc = np.asarray(k_cache)
+    vc = np.asarray(v_cache)
+    ids = np.asarray(page_ids, dtype=np.int64)
+    n = ids.shape[0]
+    block = int(np.prod(kc.shape[1:]))
+    if buffer is None:
+        out = np.zeros((2, n, block), dtype=kc.dtype)
+    else:
+        out = np.array(buffer, copy=True).reshape(2, n, block)
+    for i in range(n):
+        p = int(ids[i])
+        if 0 <= p < kc.shape[0]:
+            out[0, i] = kc[p].reshape(-1)
+            out[1, i] = vc[p].reshape(-1)
+    return out
+
+
+def import_pages(k_cache, v_cache, buffer, page_ids):
+    """Scatter buffer [2][n][block] into the listed pages; return new pool
+    copies (every page not listed keeps its bits)."""
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    ids = np.asarray(page_ids, dtype=np.int64)
+    n = ids.shape[0]
+    buf = np.asarray(buffer).reshape(2, n, -1)
+    for i in range(n):
+        p = int(ids[i])
+        if 0 <= p < kc.shape[0]:
+            kc[p] = buf[0, i].reshape(kc.shape[1:])
+            vc[p] = buf[1, i].reshape(vc.shape[1:])
+    return kc, vc

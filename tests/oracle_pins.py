@@ -508,6 +508,85 @@ def check_chunk_causality(orc):
     assert (np.abs(moved[row_of_p:] - base[row_of_p:]).max(axis=(1, 2)) > 1e-6).all()
 
 
+def check_page_export_layout(orc):
+    """Export against the pools read through flat offsets: buffer block i of
+    section 0 is page ids[i]'s K block and of section 1 its V block, in
+    order, duplicates repeated; an id outside the pool keeps the buffer's
+    previous contents."""
+    rng = np.random.default_rng(71)
+    num_pages, Hkv, P, D = 6, 2, 16, 4
+    k = rng.standard_normal((num_pages, Hkv, P, D)).astype(np.float32)
+    v = rng.standard_normal((num_pages, Hkv, D, P)).astype(np.float32)
+    ids = np.array([4, 0, 4, -1, 5, 6], dtype=np.int32)
+    block = Hkv * P * D
+    prior = np.full((2, len(ids), block), 7.5, dtype=np.float32)
+    buf = orc.export_pages(k, v, ids, prior)
+    assert buf.shape == (2, len(ids), block)
+    kf, vf = k.reshape(-1), v.reshape(-1)
+    for i, page in enumerate(ids.tolist()):
+        if not 0 <= page < num_pages:
+            assert (buf[:, i] == 7.5).all()
+            continue
+        for h in range(Hkv):
+            for t in range(P):
+                for d in range(D):
+                    assert buf[0, i, (h * P + t) * D + d] == kf[k_offset(page, h, t, d, Hkv, P, D)]
+                    assert buf[1, i, (h * D + d) * P + t] == vf[v_offset(page, h, t, d, Hkv, P, D)]
+
+
+def check_page_import_layout(orc):
+    """Import into NaN pools writes exactly the listed pages, element by
+    element through flat offsets, and nothing for an id outside the pool."""
+    rng = np.random.default_rng(72)
+    num_pages, Hkv, P, D = 7, 2, 16, 4
+    ids = np.array([3, 6, -2, 0, 9], dtype=np.int32)
+    block = Hkv * P * D
+    buf = rng.standard_normal((2, len(ids), block)).astype(np.float32)
+    k0, v0 = nan_pools(num_pages, Hkv, P, D, "f32")
+    k, v = orc.import_pages(k0, v0, buf, ids)
+    assert np.isnan(k0).all() and np.isnan(v0).all(), "inputs must not be modified"
+    kf, vf = k.reshape(-1), v.reshape(-1)
+    written = 0
+    for i, page in enumerate(ids.tolist()):
+        if not 0 <= page < num_pages:
+            continue
+        written += 1
+        for h in range(Hkv):
+            for t in range(P):
+                for d in range(D):
+                    assert kf[k_offset(page, h, t, d, Hkv, P, D)] == buf[0, i, (h * P + t) * D + d]
+                    assert vf[v_offset(page, h, t, d, Hkv, P, D)] == buf[1, i, (h * D + d) * P + t]
+    assert int(np.count_nonzero(~np.isnan(kf))) == written * block
+    assert int(np.count_nonzero(~np.isnan(vf))) == written * block
+
+
+def check_page_handoff_preserves_attention(orc):
+    """A batch moved page by page into another pool at other page ids, with
+    its block tables remapped, gathers the same tokens and decodes to the
+    same bits."""
+    wl = tiny([37, 16, 5], Hq=4, Hkv=2, D=8, dtype="bf16", seed=73)
+    k, v = fill_pools(orc, wl)
+    npg = [-(-int(L) // 16) for L in wl.context_lens]
+    ids = np.concatenate([wl.block_tables[b, :n] for b, n in enumerate(npg)]).astype(np.int32)
+    buf = orc.export_pages(k, v, ids)
+    dest_pages = len(ids) + 3
+    new_ids = np.random.default_rng(74).permutation(dest_pages)[:len(ids)].astype(np.int32)
+    k2, v2 = nan_pools(dest_pages, wl.num_kv_heads, 16, wl.head_dim, "bf16")
+    k2, v2 = orc.import_pages(k2, v2, buf, new_ids)
+    tables = np.full_like(wl.block_tables, -1)
+    at = 0
+    for b, n in enumerate(npg):
+        tables[b, :n] = new_ids[at:at + n]
+        at += n
+    for b in range(wl.num_seqs):
+        K1, V1 = orc.gather_sequence(k, v, wl.block_tables[b], wl.context_lens[b], 16)
+        K2, V2 = orc.gather_sequence(k2, v2, tables[b], wl.context_lens[b], 16)
+        assert np.array_equal(K1, K2) and np.array_equal(V1, V2)
+    a = orc.decode(wl.query, k, v, wl.block_tables, wl.context_lens, wl.scale, 16, "bf16")
+    c = orc.decode(wl.query, k2, v2, tables, wl.context_lens, wl.scale, 16, "bf16")
+    assert np.array_equal(a, c)
+
+
 ALL_CHECKS = [
     check_bf16_widening,
     check_cache_write_layout,
@@ -529,4 +608,7 @@ ALL_CHECKS = [
     check_chunk_brute_force,
     check_chunk_torch_sdpa,
     check_chunk_causality,
+    check_page_export_layout,
+    check_page_import_layout,
+    check_page_handoff_preserves_attention,
 ]

@@ -137,6 +137,36 @@ def _chunk_positions_from_zero(query, k_cache, v_cache, block_tables, context_le
     return out
 
 
+def _export_variant(swap=False, reverse=False, v_as_k=False):
+    def export_pages(k_cache, v_cache, page_ids, buffer=None):
+        kc, vc = np.asarray(k_cache), np.asarray(v_cache)
+        ids = np.asarray(page_ids, dtype=np.int64)
+        n, block = ids.shape[0], int(np.prod(kc.shape[1:]))
+        out = (np.zeros((2, n, block), dtype=kc.dtype) if buffer is None
+               else np.array(buffer, copy=True).reshape(2, n, block))
+        order = range(n - 1, -1, -1) if reverse else range(n)
+        for slot, i in enumerate(order):
+            p = int(ids[i])
+            if 0 <= p < kc.shape[0]:
+                kb = kc[p].reshape(-1)
+                vb = vc[p].transpose(0, 2, 1).reshape(-1) if v_as_k else vc[p].reshape(-1)
+                out[0, slot], out[1, slot] = (vb, kb) if swap else (kb, vb)
+        return out
+    return export_pages
+
+
+def _import_wraps_negative(k_cache, v_cache, buffer, page_ids):
+    kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+    ids = np.asarray(page_ids, dtype=np.int64)
+    buf = np.asarray(buffer).reshape(2, ids.shape[0], -1)
+    for i in range(ids.shape[0]):
+        p = int(ids[i])
+        if p < kc.shape[0]:
+            kc[p] = buf[0, i].reshape(kc.shape[1:])
+            vc[p] = buf[1, i].reshape(vc.shape[1:])
+    return kc, vc
+
+
 MUTANTS = {
     "gqa_head_modulo": ("attention", _attention_variant(group_of=lambda h, G, Hkv: h % Hkv)),
     "scale_dropped": ("attention", _attention_variant(use_scale=False)),
@@ -157,6 +187,10 @@ MUTANTS = {
     "chunk_excludes_own_token": ("causal_attention", _causal_variant(lambda p, L: max(p, 1))),
     "chunk_sees_one_token_ahead": ("causal_attention", _causal_variant(lambda p, L: p + 2)),
     "chunk_positions_from_zero": ("chunk_attention", _chunk_positions_from_zero),
+    "export_swaps_k_and_v": ("export_pages", _export_variant(swap=True)),
+    "export_reverses_page_order": ("export_pages", _export_variant(reverse=True)),
+    "export_v_in_k_layout": ("export_pages", _export_variant(v_as_k=True)),
+    "import_wraps_negative_ids": ("import_pages", _import_wraps_negative),
 }
 
 
