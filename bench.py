@@ -40,6 +40,8 @@ CHUNK_KERNEL_SOURCES = ["paged_kv_decode_pa_amd/csrc/chunk_mfma.hip",
                         "paged_kv_decode_pa_amd/csrc/page_stream.hpp",
                         "paged_kv_decode_pa_amd/csrc/pa_device.hpp"]
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+TRANSFER_METRIC = ("KV page hand-off: export every page of the batch to one buffer, import it "
+                   "into another pool; GB/s read + written, 1 GPU")
 CHUNK_METRIC = ("multi-token causal attention over the paged cache (draft verification / "
                 "chunked prefill): query tokens/s, 1 GPU")
 
@@ -77,6 +79,9 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--transfer", action="store_true",
+                    help="time pa_export_pages + pa_import_pages of every page of the batch "
+                         "instead of the decode step")
     ap.add_argument("--chunk", type=int, default=0, metavar="Q",
                     help="time pa_chunk_attention with Q new tokens per sequence instead of the "
                          "decode step (the cache write of the Q tokens, then the attention)")
@@ -482,6 +487,95 @@ def run_chunk_config(cid, args):
     }
 
 
+def run_transfer_config(cid, args):
+    import torch
+
+    import paged_kv_decode_pa_amd as pa
+    from workloads import config_by_id, make_workload
+
+    cfg = config_by_id(cid)
+    wl = make_workload(cfg, share_prefix=not args.unshared)
+    dev = torch.device("cuda:0")
+    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+
+    def up(a):
+        if wl.dtype == "f32":
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    P, Hkv, D = wl.page_size, wl.num_kv_heads, wl.head_dim
+    k_cache = torch.full((wl.num_pages, Hkv, P, D), float("nan"), dtype=dt, device=dev)
+    v_cache = torch.full((wl.num_pages, Hkv, D, P), float("nan"), dtype=dt, device=dev)
+    pa.pa_reshape_and_cache(up(wl.prefill_key), up(wl.prefill_value), k_cache, v_cache,
+                            torch.from_numpy(wl.prefill_slots).to(dev))
+    pa.pa_reshape_and_cache(up(wl.new_key), up(wl.new_value), k_cache, v_cache,
+                            torch.from_numpy(wl.new_slots).to(dev))
+    n_of = (wl.context_lens.astype(np.int64) + P - 1) // P
+    used = np.unique(np.concatenate([wl.block_tables[b, :n_of[b]] for b in range(wl.num_seqs)]))
+    n = len(used)
+    ids = torch.from_numpy(used.astype(np.int32)).to(dev)
+    dest = torch.from_numpy(np.random.default_rng(200 + cid).permutation(wl.num_pages)[:n]
+                            .astype(np.int32)).to(dev)
+    block = Hkv * P * D
+    buf = torch.empty((2, n, block), dtype=dt, device=dev)
+    k2 = torch.full_like(k_cache, float("nan"))
+    v2 = torch.full_like(v_cache, float("nan"))
+    flush_buf = None if args.no_flush else torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        pa.pa_export_pages(buf, k_cache, v_cache, ids)
+        if ev:
+            ev[1].record()
+        pa.pa_import_pages(buf, k2, v2, dest)
+        if ev:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        if flush_buf is not None:
+            flush_buf.sum()
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        if flush_buf is not None:
+            flush_buf.sum()
+        step(ev[k])
+    torch.cuda.synchronize()
+    if args.copy_calibration:
+        copy_calibration(dev)
+    if not torch.equal(k2[dest.long()].view(torch.int16), k_cache[ids.long()].view(torch.int16)):
+        raise RuntimeError("imported K pages differ from the exported ones")
+    exp_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    imp_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    step_ms = [e[0].elapsed_time(e[2]) for e in ev]
+    moved = 2 * n * block * wl.elem_bytes          # K and V blocks, one direction
+    t_exp = float(np.mean(exp_ms)) * 1e-3
+    t_step = float(np.mean(step_ms)) * 1e-3
+    achieved = 2 * moved / t_exp / 1e9             # read + written by the export
+    return {
+        "metric": TRANSFER_METRIC,
+        "value": round(4 * moved / t_step / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[cid] + f"; all {n} pages in use exported and "
+                   "imported at permuted ids", "pages": n, "bytes_per_page_kv": 2 * block * wl.elem_bytes,
+                   "cache_flush_between_steps": flush_buf is not None,
+                   "parallelism": "none (1 GPU)"},
+        "kernels_ms": {"export": stats(exp_ms), "import": stats(imp_ms), "step": stats(step_ms)},
+        "roofline": {"bound": "hbm", "kernel": "page_copy_kernel<true> (export)",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": 2 * moved,
+                     "mean_launch_us": round(t_exp * 1e6, 2)},
+    }
+
+
 def cpu_baseline(wl, budget_s, nb, t_step_gpu):
     """The fp64 oracle, as it stands, on a bounded sample of the same batch:
     whole sequences in batch order until the time budget is spent."""
@@ -535,6 +629,9 @@ def main():
     pa.load()
     if args.chunk:
         print(json.dumps(run_chunk_config(args.config, args)), flush=True)
+        return
+    if args.transfer:
+        print(json.dumps(run_transfer_config(args.config, args)), flush=True)
         return
     others = [c for c in (1, 2, 3, 4, 5) if c != args.config] if args.all else []
     for cid in others:

@@ -222,6 +222,44 @@ int pa_decode_reduce(void* out, const float* partial_out, const float* partial_m
                      int num_q_heads, int head_dim, int partition_size,
                      int max_num_partitions, int dtype, void* stream);
 
+/*
+ * pa_export_pages / pa_import_pages — move whole KV pages between a pool and
+ * one contiguous buffer: the on-GPU half of handing a sequence's KV cache
+ * from the engine that computed it to the one that decodes it (llm-d blog
+ * post, disaggregated prefill/decode section: the KV computed by the prefill
+ * pods is transferred to the decode pods; the network half is not here).
+ *
+ *   buffer      [2][num_ids][num_kv_heads * 16 * head_dim] elements of dtype:
+ *               section 0 holds the K blocks, section 1 the V blocks, of
+ *               page_ids[0], page_ids[1], ... in that order.  Each block is
+ *               the pool page's own bytes (K [Hkv][16][D], V [Hkv][D][16]),
+ *               so a receiving pool of the same shape takes it unchanged.
+ *               Export writes it; import reads it.  16-byte aligned.
+ *   buffer_bytes  size of `buffer`; must be at least
+ *               2 * num_ids * num_kv_heads * 16 * head_dim * element size.
+ *   page_ids    [num_ids] int32, device (a block-table row serves directly:
+ *               a sequence of length L exports its first ceil(L / 16) ids).
+ *   k_cache, v_cache, num_kv_heads, head_dim, page_size, num_pages, dtype:
+ *               the pool, as for pa_reshape_and_cache.
+ *
+ * Bit copies: slots past a sequence's length travel as they are (they are
+ * never read by attention).  An id outside [0, num_pages) is skipped: export
+ * leaves that id's buffer blocks unwritten, import writes nothing for it.
+ * Import writes exactly the listed pages; ids must be distinct, and no other
+ * call may read or write those pages until the stream passes this one (the
+ * single-writer rule of pa_reshape_and_cache).  num_ids == 0 is a no-op that
+ * examines no pointer (an empty tensor's address may be NULL).
+ * Errors: a NULL pointer, a negative count, a short buffer or misalignment
+ * returns PA_ERR_INVALID_ARGUMENT; head_dim, page_size or dtype outside the
+ * supported set returns PA_ERR_UNSUPPORTED.
+ */
+int pa_export_pages(void* buffer, int64_t buffer_bytes, const void* k_cache, const void* v_cache,
+                    const int32_t* page_ids, int64_t num_ids, int num_kv_heads, int head_dim,
+                    int page_size, int64_t num_pages, int dtype, void* stream);
+int pa_import_pages(const void* buffer, int64_t buffer_bytes, void* k_cache, void* v_cache,
+                    const int32_t* page_ids, int64_t num_ids, int num_kv_heads, int head_dim,
+                    int page_size, int64_t num_pages, int dtype, void* stream);
+
 /* Human-readable name of a pa_status value (static storage). */
 const char* pa_status_string(int status);
 

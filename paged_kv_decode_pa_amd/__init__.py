@@ -12,6 +12,8 @@ from ._lib import (  # noqa: F401
     pa_decode,
     pa_decode_reduce,
     pa_decode_valu,
+    pa_export_pages,
+    pa_import_pages,
     pa_reshape_and_cache,
     status_string,
     version,

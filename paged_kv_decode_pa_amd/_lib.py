@@ -41,6 +41,10 @@ _SIGNATURES = {
                            _f32, _i32, _c_void_p],
     "pa_decode_reduce": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
                          _i32, _i32, _i32, _c_void_p],
+    "pa_export_pages": [_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _i32,
+                        _i64, _i32, _c_void_p],
+    "pa_import_pages": [_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _i32,
+                        _i64, _i32, _c_void_p],
     "pa_status_string": [_i32],
     "pa_version": [],
 }
@@ -184,6 +188,33 @@ def pa_chunk_attention(out, query, k_cache, v_cache, block_tables, context_lens,
         _ptr(context_lens), _ptr(query_start), B, T, int(max_query_len), Hq, Hkv, D, PAGE_SIZE,
         block_tables.shape[1], k_cache.shape[0], float(scale), _dtype_code(query),
         _stream(stream)))
+
+
+def _page_copy(name, buffer, k_cache, v_cache, page_ids, stream):
+    n = page_ids.shape[0]
+    Hkv, D = k_cache.shape[1], k_cache.shape[3]
+    if k_cache.shape[2] != PAGE_SIZE or v_cache.shape != (k_cache.shape[0], Hkv, D, PAGE_SIZE):
+        raise ValueError("k_cache / v_cache shapes disagree")
+    if not (buffer.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("buffer and pools must share one dtype")
+    if page_ids.dim() != 1:
+        raise ValueError("page_ids must be one-dimensional")
+    lib = load()
+    _check(name, getattr(lib, name)(
+        _ptr(buffer), buffer.numel() * buffer.element_size(), _ptr(k_cache), _ptr(v_cache),
+        _ptr(page_ids), n, Hkv, D, PAGE_SIZE, k_cache.shape[0], _dtype_code(k_cache),
+        _stream(stream)))
+
+
+def pa_export_pages(buffer, k_cache, v_cache, page_ids, stream=None) -> None:
+    """Gather pages page_ids (int32 [n]) into buffer [2][n][Hkv][16*D]: the K
+    blocks, then the V blocks, each in the pool's own page layout."""
+    _page_copy("pa_export_pages", buffer, k_cache, v_cache, page_ids, stream)
+
+
+def pa_import_pages(buffer, k_cache, v_cache, page_ids, stream=None) -> None:
+    """Scatter a buffer laid out as pa_export_pages writes it into pages page_ids."""
+    _page_copy("pa_import_pages", buffer, k_cache, v_cache, page_ids, stream)
 
 
 def pa_decode_valu(out, query, k_cache, v_cache, block_tables, context_lens, scale,

@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpa.so")
 SOURCES = ["pa_api.hip", "reshape_and_cache.hip", "decode_mfma.hip", "decode_valu.hip",
-           "decode_reduce.hip", "chunk_mfma.hip"]
+           "decode_reduce.hip", "chunk_mfma.hip", "page_transfer.hip"]
 ARCH = "gfx950"
 
 

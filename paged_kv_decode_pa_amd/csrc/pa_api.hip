@@ -15,6 +15,9 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
                                     int num_kv_heads, int head_dim, int64_t num_pages, bool bf16,
                                     hipStream_t stream);
 hipError_t launch_chunk_attention(const ChunkParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_page_copy(bool export_dir, void* buf, void* k_cache, void* v_cache,
+                            const int32_t* page_ids, int64_t num_ids, int64_t num_pages,
+                            int64_t block_bytes, hipStream_t stream);
 hipError_t launch_decode_reduce(void* out, const float* part_out, const float* part_max,
                                 const float* part_sum, const int32_t* context_lens, int num_seqs,
                                 int num_q_heads, int head_dim, int partition_size, int max_parts,
@@ -92,6 +95,26 @@ int decode_impl(DecodeKernel which, void* out, const void* query, const void* k_
   const hipError_t err = (bf16 && which == DecodeKernel::kAuto)
                              ? pa::launch_decode_mfma(p, head_dim, s)
                              : pa::launch_decode_valu(p, head_dim, bf16, s);
+  return err == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int page_copy_impl(bool export_dir, void* buffer, int64_t buffer_bytes, void* k_cache,
+                   void* v_cache, const int32_t* page_ids, int64_t num_ids, int num_kv_heads,
+                   int head_dim, int page_size, int64_t num_pages, int dtype, void* stream) {
+  if (num_ids < 0 || buffer_bytes < 0 || num_kv_heads <= 0 || num_pages <= 0)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (int s = check_common(head_dim, page_size, dtype)) return s;
+  if (num_ids > INT_MAX / 2) return PA_ERR_UNSUPPORTED;  // two workgroups per page
+  const int64_t esz = dtype == PA_DTYPE_BF16 ? 2 : 4;
+  const int64_t block_bytes = int64_t(num_kv_heads) * page_size * head_dim * esz;
+  if (num_ids > 0 && buffer_bytes / 2 / num_ids < block_bytes) return PA_ERR_INVALID_ARGUMENT;
+  if (num_ids == 0) return PA_OK;  // an empty list examines no pointer
+  if (!buffer || !k_cache || !v_cache || !page_ids) return PA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(buffer) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_ERR_INVALID_ARGUMENT;
+  const hipError_t err = pa::launch_page_copy(export_dir, buffer, k_cache, v_cache, page_ids,
+                                              num_ids, num_pages, block_bytes,
+                                              static_cast<hipStream_t>(stream));
   return err == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
@@ -175,6 +198,22 @@ int pa_chunk_attention(void* out, const void* query, const void* k_cache, const 
   p.num_units = int(units);
   const hipError_t err = pa::launch_chunk_attention(p, head_dim, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int pa_export_pages(void* buffer, int64_t buffer_bytes, const void* k_cache, const void* v_cache,
+                    const int32_t* page_ids, int64_t num_ids, int num_kv_heads, int head_dim,
+                    int page_size, int64_t num_pages, int dtype, void* stream) {
+  return page_copy_impl(true, buffer, buffer_bytes, const_cast<void*>(k_cache),
+                        const_cast<void*>(v_cache), page_ids, num_ids, num_kv_heads, head_dim,
+                        page_size, num_pages, dtype, stream);
+}
+
+int pa_import_pages(const void* buffer, int64_t buffer_bytes, void* k_cache, void* v_cache,
+                    const int32_t* page_ids, int64_t num_ids, int num_kv_heads, int head_dim,
+                    int page_size, int64_t num_pages, int dtype, void* stream) {
+  return page_copy_impl(false, const_cast<void*>(buffer), buffer_bytes, k_cache, v_cache,
+                        page_ids, num_ids, num_kv_heads, head_dim, page_size, num_pages, dtype,
+                        stream);
 }
 
 int pa_decode_valu(void* out, const void* query, const void* k_cache, const void* v_cache,

@@ -208,3 +208,41 @@ def test_binding_raises_on_error_status():
     with pytest.raises(pa.PaError) as e:
         _lib._check("pa_decode", UNSUP)
     assert e.value.status == UNSUP and "PA_ERR_UNSUPPORTED" in str(e.value)
+
+
+def transfer_args(**kw):
+    block = 8 * 16 * 128 * 2
+    a = dict(buffer=P, buffer_bytes=2 * 10 * block, k_cache=P, v_cache=P, page_ids=P, num_ids=10,
+             num_kv_heads=8, head_dim=128, page_size=16, num_pages=64, dtype=BF16, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+TRANSFER_CASES = [
+    ("null_buffer", dict(buffer=None), INVAL),
+    ("null_k_cache", dict(k_cache=None), INVAL),
+    ("null_v_cache", dict(v_cache=None), INVAL),
+    ("null_ids", dict(page_ids=None), INVAL),
+    ("misaligned_buffer", dict(buffer=P + 8), INVAL),
+    ("short_buffer", dict(buffer_bytes=2 * 10 * 8 * 16 * 128 * 2 - 1), INVAL),
+    ("negative_ids", dict(num_ids=-1), INVAL),
+    ("negative_buffer_bytes", dict(buffer_bytes=-1), INVAL),
+    ("zero_kv_heads", dict(num_kv_heads=0), INVAL),
+    ("zero_pool", dict(num_pages=0), INVAL),
+    ("head_dim_96", dict(head_dim=96), UNSUP),
+    ("page_size_32", dict(page_size=32), UNSUP),
+    ("unknown_dtype", dict(dtype=7), UNSUP),
+    ("f32_needs_twice_the_bytes", dict(dtype=F32), INVAL),
+    ("too_many_ids", dict(num_ids=2**31, buffer_bytes=2**62), UNSUP),
+]
+
+
+@pytest.mark.parametrize("fn", ["pa_export_pages", "pa_import_pages"])
+@pytest.mark.parametrize("name,kw,want", TRANSFER_CASES, ids=[c[0] for c in TRANSFER_CASES])
+def test_page_transfer_rejects(fn, name, kw, want):
+    assert getattr(pa.load(), fn)(*transfer_args(**kw)) == want
+
+
+@pytest.mark.parametrize("fn", ["pa_export_pages", "pa_import_pages"])
+def test_page_transfer_empty_is_a_noop(fn):
+    assert getattr(pa.load(), fn)(*transfer_args(num_ids=0, buffer_bytes=0)) == OK
