@@ -18,3 +18,4 @@ from ._lib import (  # noqa: F401
     status_string,
     version,
 )
+from .pager import Pager, PagerError, page_hash  # noqa: F401,E402

@@ -13,6 +13,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpa.so")
+PAGER_LIB = os.path.join(PKG, "libpa_pager.so")
+PAGER_SOURCES = ["pager.cpp"]
 SOURCES = ["pa_api.hip", "reshape_and_cache.hip", "decode_mfma.hip", "decode_valu.hip",
            "decode_reduce.hip", "chunk_mfma.hip", "page_transfer.hip"]
 ARCH = "gfx950"
@@ -47,8 +49,28 @@ def device_asm_command(source: str, out: str) -> list:
     return [*flags, "--cuda-device-only", "-S", os.path.join(CSRC, source)]
 
 
+def pager_command(out: str = PAGER_LIB) -> list:
+    """The host-only page pool owner: plain C++17, no HIP."""
+    cxx = os.environ.get("CXX", "g++")
+    return [cxx, "-std=c++17", "-O2", "-Wall", "-Wextra", "-fPIC", "-shared", f"-I{INCLUDE}",
+            *[os.path.join(CSRC, s) for s in PAGER_SOURCES], "-o", out]
+
+
+def build_pager(verbose: bool = False) -> str:
+    tmp = PAGER_LIB + ".tmp"
+    cmd = pager_command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"pager build failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, PAGER_LIB)
+    return PAGER_LIB
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source into libpa.so (always recompiles)."""
+    """Compile every source into libpa.so and libpa_pager.so (always recompiles)."""
+    build_pager(verbose)
     tmp = LIB + ".tmp"
     cmd = command(tmp)
     if verbose:

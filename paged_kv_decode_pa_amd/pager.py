@@ -1,0 +1,156 @@
+"""Python face of libpa_pager.so (include/pa_pager.h): the host-side owner of
+the KV page pool.  Marshalling only; the policy lives in the C++ library."""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import build as _build
+
+PAGER_LIB_PATH = _build.PAGER_LIB
+
+OK, INVALID_ARGUMENT, OUT_OF_PAGES, UNKNOWN_SEQUENCE, SEQUENCE_EXISTS, SEQUENCE_FULL = range(6)
+EVENT_STORED, EVENT_REMOVED = 0, 1
+_NAMES = ["PA_PAGER_OK", "PA_PAGER_INVALID_ARGUMENT", "PA_PAGER_OUT_OF_PAGES",
+          "PA_PAGER_UNKNOWN_SEQUENCE", "PA_PAGER_SEQUENCE_EXISTS", "PA_PAGER_SEQUENCE_FULL"]
+
+
+class PagerError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        name = _NAMES[status] if 0 <= status < len(_NAMES) else str(status)
+        super().__init__(f"{fn} failed: {name}")
+
+
+class _Stats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "num_pages", "in_use", "cached_free", "empty_free", "registered", "live_sequences",
+        "prefix_hit_tokens", "evictions", "cow_copies")]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32P = ctypes.POINTER(ctypes.c_int32)
+_I64P = ctypes.POINTER(ctypes.c_int64)
+_U64P = ctypes.POINTER(ctypes.c_uint64)
+
+
+def load(path: str = PAGER_LIB_PATH) -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m paged_kv_decode_pa_amd.build`")
+    lib = ctypes.CDLL(path)
+    sig = {
+        "pa_pager_create": ([ctypes.c_int64, ctypes.c_int, ctypes.c_int], _P),
+        "pa_pager_destroy": ([_P], None),
+        "pa_pager_add_sequence": ([_P, ctypes.c_int64, _I32P, ctypes.c_int64, _I64P, _I64P],
+                                  ctypes.c_int),
+        "pa_pager_append": ([_P, ctypes.c_int64, ctypes.c_int32, _I64P, _I64P, _I64P],
+                            ctypes.c_int),
+        "pa_pager_fork": ([_P, ctypes.c_int64, ctypes.c_int64], ctypes.c_int),
+        "pa_pager_free_sequence": ([_P, ctypes.c_int64], ctypes.c_int),
+        "pa_pager_block_tables": ([_P, _I64P, ctypes.c_int64, _I32P, _I32P], ctypes.c_int),
+        "pa_pager_get_stats": ([_P, ctypes.POINTER(_Stats)], ctypes.c_int),
+        "pa_pager_drain_events": ([_P, _I32P, _I64P, _U64P, ctypes.c_int64, _I64P], ctypes.c_int),
+        "pa_pager_page_hash": ([ctypes.c_uint64, _I32P, ctypes.c_int], ctypes.c_uint64),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def page_hash(parent: int, tokens: Sequence[int]) -> int:
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    return int(load().pa_pager_page_hash(parent, _ptr(t, ctypes.c_int32), len(t)))
+
+
+class Pager:
+    """Owner of a pool of `num_pages` pages of `page_size` tokens."""
+
+    def __init__(self, num_pages: int, page_size: int = 16, max_pages_per_seq: int = 512):
+        self._lib = load()
+        self._h = self._lib.pa_pager_create(num_pages, page_size, max_pages_per_seq)
+        if not self._h:
+            raise ValueError("bad pager shape")
+        self.page_size = page_size
+        self.max_pages_per_seq = max_pages_per_seq
+
+    def close(self) -> None:
+        if self._h:
+            self._lib.pa_pager_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001  (interpreter shutdown)
+            pass
+
+    def _check(self, fn: str, status: int) -> None:
+        if status != OK:
+            raise PagerError(fn, status)
+
+    def add_sequence(self, seq_id: int, tokens: Sequence[int]) -> Tuple[np.ndarray, int]:
+        """Slot of every prompt token and how many leading tokens are cached."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        slots = np.empty(len(t), dtype=np.int64)
+        cached = ctypes.c_int64(0)
+        self._check("pa_pager_add_sequence", self._lib.pa_pager_add_sequence(
+            self._h, seq_id, _ptr(t, ctypes.c_int32), len(t), _ptr(slots, ctypes.c_int64),
+            ctypes.byref(cached)))
+        return slots, cached.value
+
+    def append(self, seq_id: int, token: int) -> Tuple[int, Optional[Tuple[int, int]]]:
+        """Slot of one new token, and the (src, dst) page copy to make first, if any."""
+        slot, src, dst = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        self._check("pa_pager_append", self._lib.pa_pager_append(
+            self._h, seq_id, token, ctypes.byref(slot), ctypes.byref(src), ctypes.byref(dst)))
+        return slot.value, (None if src.value < 0 else (src.value, dst.value))
+
+    def fork(self, parent: int, child: int) -> None:
+        self._check("pa_pager_fork", self._lib.pa_pager_fork(self._h, parent, child))
+
+    def free_sequence(self, seq_id: int) -> None:
+        self._check("pa_pager_free_sequence", self._lib.pa_pager_free_sequence(self._h, seq_id))
+
+    def block_tables(self, seq_ids: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
+        """int32 [n][max_pages_per_seq] (padded with -1) and int32 [n]."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        tables = np.empty((len(ids), self.max_pages_per_seq), dtype=np.int32)
+        lens = np.empty(len(ids), dtype=np.int32)
+        self._check("pa_pager_block_tables", self._lib.pa_pager_block_tables(
+            self._h, _ptr(ids, ctypes.c_int64), len(ids), _ptr(tables, ctypes.c_int32),
+            _ptr(lens, ctypes.c_int32)))
+        return tables, lens
+
+    def stats(self) -> dict:
+        s = _Stats()
+        self._check("pa_pager_get_stats", self._lib.pa_pager_get_stats(self._h, ctypes.byref(s)))
+        return {name: getattr(s, name) for name, _ in _Stats._fields_}
+
+    def drain_events(self, capacity: int = 4096) -> List[Tuple[int, int, int]]:
+        """Pending (kind, page, hash) events, oldest first."""
+        out: List[Tuple[int, int, int]] = []
+        kinds = np.empty(capacity, dtype=np.int32)
+        pages = np.empty(capacity, dtype=np.int64)
+        hashes = np.empty(capacity, dtype=np.uint64)
+        while True:
+            n = ctypes.c_int64()
+            self._check("pa_pager_drain_events", self._lib.pa_pager_drain_events(
+                self._h, _ptr(kinds, ctypes.c_int32), _ptr(pages, ctypes.c_int64),
+                _ptr(hashes, ctypes.c_uint64), capacity, ctypes.byref(n)))
+            out += [(int(kinds[i]), int(pages[i]), int(hashes[i])) for i in range(n.value)]
+            if n.value < capacity:
+                return out
