@@ -18,6 +18,7 @@ the other workloads go to stderr first.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -42,6 +43,8 @@ CHUNK_KERNEL_SOURCES = ["paged_kv_decode_pa_amd/csrc/chunk_mfma.hip",
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 TRANSFER_METRIC = ("KV page hand-off: export every page of the batch to one buffer, import it "
                    "into another pool; GB/s read + written, 1 GPU")
+PAGER_METRIC = ("host page-pool owner: decode steps/s of bookkeeping (one append per "
+                "sequence + the batch's block tables), 1 host thread")
 CHUNK_METRIC = ("multi-token causal attention over the paged cache (draft verification / "
                 "chunked prefill): query tokens/s, 1 GPU")
 
@@ -82,6 +85,9 @@ def parse_args():
     ap.add_argument("--transfer", action="store_true",
                     help="time pa_export_pages + pa_import_pages of every page of the batch "
                          "instead of the decode step")
+    ap.add_argument("--pager", action="store_true",
+                    help="time the host page-pool owner (no GPU): admitting the batch's "
+                         "prompts, then decode-step appends and block tables")
     ap.add_argument("--chunk", type=int, default=0, metavar="Q",
                     help="time pa_chunk_attention with Q new tokens per sequence instead of the "
                          "decode step (the cache write of the Q tokens, then the attention)")
@@ -576,6 +582,114 @@ def run_transfer_config(cid, args):
     }
 
 
+def run_pager_config(cid, args):
+    """The native pager on the workload's shapes: every sequence's prompt
+    (its cached tokens) admitted with synthetic token ids (sequences of a
+    prefix group share their prefix ids, so the prefix pages are reused),
+    then decode steps of one append per sequence plus the block tables; the
+    policy model in oracle.pager timed on a bounded sample beside it."""
+    import oracle.pager as opager
+
+    import paged_kv_decode_pa_amd as pa
+    from workloads import config_by_id, make_workload
+
+    cfg = config_by_id(cid)
+    wl = make_workload(cfg, share_prefix=not args.unshared)
+    rng = np.random.default_rng(300 + cid)
+    B, P = wl.num_seqs, wl.page_size
+    lens = wl.context_lens.astype(np.int64) - 1   # prompt = the cached tokens
+    shared = cfg.prefix_group_size > 0 and not args.unshared
+    prefix_len = cfg.prefix_tokens if shared else 0
+    stems = {}
+    prompts = []
+    for b in range(B):
+        g = b // cfg.prefix_group_size if shared else -1 - b
+        if g not in stems:
+            stems[g] = rng.integers(0, 128000, size=prefix_len).astype(np.int32)
+        tail = rng.integers(0, 128000, size=int(lens[b]) - len(stems[g])).astype(np.int32)
+        prompts.append(np.concatenate([stems[g], tail]))
+    steps = max(args.steps, 1) * 4
+    grow = 2 * steps // P + 2  # pages each sequence gains over the two timed loops
+    max_pages = int(wl.block_tables.shape[1]) + grow
+    num_pages = int(wl.num_pages) + B * grow
+
+    def native():
+        pg = pa.Pager(num_pages, P, max_pages)
+        t0 = time.perf_counter()
+        for b in range(B):
+            pg.add_sequence(b, prompts[b])
+        t_admit = time.perf_counter() - t0
+        ids = np.arange(B, dtype=np.int64)
+        toks = rng.integers(0, 128000, size=(steps, B)).astype(np.int32)
+        app = tuple(np.empty(B, dtype=np.int64) for _ in range(3))
+        tab = (np.empty((B, max_pages), dtype=np.int32), np.empty(B, dtype=np.int32))
+        # The engine's path: the library entry points called with the step's
+        # buffers' addresses computed once.
+        lib, h = pg._lib, pg._h
+        a_ids, a_tok, a_tab, a_len = ids.ctypes.data, toks.ctypes.data, tab[0].ctypes.data, \
+            tab[1].ctypes.data
+        a_out = [x.ctypes.data for x in app]
+        done = ctypes.c_int64()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            if lib.pa_pager_append_batch(h, a_ids, a_tok + 4 * B * k, B, *a_out,
+                                         ctypes.byref(done)):
+                raise RuntimeError("append_batch failed")
+            if lib.pa_pager_block_tables(h, a_ids, B, a_tab, a_len):
+                raise RuntimeError("block_tables failed")
+        t_dec = (time.perf_counter() - t0) / steps
+        # The same through the convenience binding (per-call marshalling).
+        t0 = time.perf_counter()
+        for k in range(steps):
+            pg.append_batch(ids, toks[k], out=app)
+            pg.block_tables(ids, out=tab)
+        t_py = (time.perf_counter() - t0) / steps
+        return t_admit, t_dec, t_py, pg.stats()
+
+    def model(n_seqs, n_steps):
+        m = opager.PagerModel(num_pages, P, max_pages)
+        t0 = time.perf_counter()
+        for b in range(n_seqs):
+            m.add_sequence(b, prompts[b].tolist())
+        t_admit = time.perf_counter() - t0
+        ids = list(range(n_seqs))
+        t0 = time.perf_counter()
+        for k in range(n_steps):
+            for b in ids:
+                m.append(b, 1)
+            m.block_tables(ids)
+        return t_admit, (time.perf_counter() - t0) / n_steps
+
+    native()  # warm-up (page faults, allocator)
+    t_admit, t_dec, t_py, st = native()
+    n_m = min(B, 8)
+    m_admit, m_dec = model(n_m, 3)
+    admitted = int(lens.sum())
+    return {
+        "metric": PAGER_METRIC,
+        "value": round(1.0 / t_dec, 1),
+        "unit": "steps/s",
+        "n_gpus": 0, "steps": steps, "warmup": 1,
+        "ms_per_step": round(t_dec * 1e3, 4),
+        "higher_is_better": True, "scaling": "none", "vs_baseline": None,
+        "dtype": "int32", "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[cid] + "; prompts = the cached tokens, token ids "
+                   "synthetic, shared prefix ids per group", "batch": B, "page_size": P,
+                   "num_pages": num_pages, "parallelism": "none (host)"},
+        "admission": {"tokens": admitted, "seconds": round(t_admit, 6),
+                      "tokens_per_s": round(admitted / t_admit, 1),
+                      "prefix_hit_tokens": st["prefix_hit_tokens"]},
+        "decode_step_us": round(t_dec * 1e6, 2),
+        "decode_step_us_via_python_binding": round(t_py * 1e6, 2),
+        "stats_after": st,
+        "cpu_baseline": {"value": round(1.0 / (m_dec * B / n_m), 2), "unit": "steps/s",
+                         "cores": 1, "kind": "oracle",
+                         "sample": f"the policy model (oracle.pager) on the first {n_m} "
+                                   f"sequences, 3 decode steps, scaled to {B} sequences; "
+                                   f"admission {int(lens[:n_m].sum()) / m_admit:.0f} tokens/s"},
+    }
+
+
 def cpu_baseline(wl, budget_s, nb, t_step_gpu):
     """The fp64 oracle, as it stands, on a bounded sample of the same batch:
     whole sequences in batch order until the time budget is spent."""
@@ -619,6 +733,9 @@ def main():
               "(decode attention shards by sequence or kv head with no exchange)",
               file=sys.stderr)
         sys.exit(2)
+    if args.pager:
+        print(json.dumps(run_pager_config(args.config, args)), flush=True)
+        return
     import torch
 
     if not torch.cuda.is_available():

@@ -98,6 +98,14 @@ int pa_pager_add_sequence(pa_pager* pager, int64_t seq_id, const int32_t* tokens
 int pa_pager_append(pa_pager* pager, int64_t seq_id, int32_t token, int64_t* slot,
                     int64_t* copy_src, int64_t* copy_dst);
 
+/* One decode step's appends: token tokens[i] to sequence seq_ids[i], in
+ * order, with slot and copy results as for pa_pager_append (arrays of n,
+ * host memory).  Stops at the first failing append and returns its status;
+ * *num_done receives how many appends were made (all of them on success). */
+int pa_pager_append_batch(pa_pager* pager, const int64_t* seq_ids, const int32_t* tokens,
+                          int64_t n, int64_t* slots, int64_t* copy_src, int64_t* copy_dst,
+                          int64_t* num_done);
+
 /* `child` starts as a copy of `parent` sharing all of its pages. */
 int pa_pager_fork(pa_pager* pager, int64_t parent, int64_t child);
 

@@ -234,6 +234,21 @@ int pa_pager_append(pa_pager* pg, int64_t seq_id, int32_t token, int64_t* slot,
   return PA_PAGER_OK;
 }
 
+int pa_pager_append_batch(pa_pager* pg, const int64_t* seq_ids, const int32_t* tokens,
+                          int64_t n, int64_t* slots, int64_t* copy_src, int64_t* copy_dst,
+                          int64_t* num_done) {
+  if (!pg || n < 0 || !num_done ||
+      (n > 0 && (!seq_ids || !tokens || !slots || !copy_src || !copy_dst)))
+    return PA_PAGER_INVALID_ARGUMENT;
+  *num_done = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    const int st = pa_pager_append(pg, seq_ids[i], tokens[i], slots + i, copy_src + i, copy_dst + i);
+    if (st != PA_PAGER_OK) return st;
+    *num_done = i + 1;
+  }
+  return PA_PAGER_OK;
+}
+
 int pa_pager_fork(pa_pager* pg, int64_t parent, int64_t child) {
   if (!pg) return PA_PAGER_INVALID_ARGUMENT;
   auto it = pg->seqs.find(parent);
@@ -259,13 +274,17 @@ int pa_pager_block_tables(const pa_pager* pg, const int64_t* seq_ids, int64_t n,
                           int32_t* context_lens) {
   if (!pg || n < 0 || (n > 0 && (!seq_ids || !tables || !context_lens)))
     return PA_PAGER_INVALID_ARGUMENT;
-  for (int64_t i = 0; i < n; ++i)
-    if (!pg->seqs.count(seq_ids[i])) return PA_PAGER_UNKNOWN_SEQUENCE;
+  std::vector<const Sequence*> found(size_t(n), nullptr);
   for (int64_t i = 0; i < n; ++i) {
-    const Sequence& s = pg->seqs.at(seq_ids[i]);
+    auto it = pg->seqs.find(seq_ids[i]);
+    if (it == pg->seqs.end()) return PA_PAGER_UNKNOWN_SEQUENCE;  // nothing written
+    found[size_t(i)] = &it->second;
+  }
+  for (int64_t i = 0; i < n; ++i) {
+    const Sequence& s = *found[size_t(i)];
     int32_t* row = tables + i * pg->max_pages;
-    for (int j = 0; j < pg->max_pages; ++j)
-      row[j] = j < int(s.pages.size()) ? s.pages[size_t(j)] : -1;
+    std::copy(s.pages.begin(), s.pages.end(), row);
+    std::fill(row + s.pages.size(), row + pg->max_pages, -1);
     context_lens[i] = int32_t(s.len);
   }
   return PA_PAGER_OK;

@@ -33,9 +33,9 @@ class _Stats(ctypes.Structure):
 
 _lib = None
 _P = ctypes.c_void_p
-_I32P = ctypes.POINTER(ctypes.c_int32)
-_I64P = ctypes.POINTER(ctypes.c_int64)
-_U64P = ctypes.POINTER(ctypes.c_uint64)
+# Host arrays travel as plain addresses (numpy's .ctypes.data): converting
+# to typed ctypes pointers costs microseconds per argument.
+_I32P = _I64P = _U64P = ctypes.c_void_p
 
 
 def load(path: str = PAGER_LIB_PATH) -> ctypes.CDLL:
@@ -52,6 +52,8 @@ def load(path: str = PAGER_LIB_PATH) -> ctypes.CDLL:
                                   ctypes.c_int),
         "pa_pager_append": ([_P, ctypes.c_int64, ctypes.c_int32, _I64P, _I64P, _I64P],
                             ctypes.c_int),
+        "pa_pager_append_batch": ([_P, _I64P, _I32P, ctypes.c_int64, _I64P, _I64P, _I64P, _I64P],
+                                  ctypes.c_int),
         "pa_pager_fork": ([_P, ctypes.c_int64, ctypes.c_int64], ctypes.c_int),
         "pa_pager_free_sequence": ([_P, ctypes.c_int64], ctypes.c_int),
         "pa_pager_block_tables": ([_P, _I64P, ctypes.c_int64, _I32P, _I32P], ctypes.c_int),
@@ -67,8 +69,8 @@ def load(path: str = PAGER_LIB_PATH) -> ctypes.CDLL:
     return lib
 
 
-def _ptr(a: np.ndarray, ctype):
-    return a.ctypes.data_as(ctypes.POINTER(ctype))
+def _ptr(a: np.ndarray, ctype=None):
+    return a.ctypes.data
 
 
 def page_hash(parent: int, tokens: Sequence[int]) -> int:
@@ -119,17 +121,54 @@ class Pager:
             self._h, seq_id, token, ctypes.byref(slot), ctypes.byref(src), ctypes.byref(dst)))
         return slot.value, (None if src.value < 0 else (src.value, dst.value))
 
+    def append_batch(self, seq_ids, tokens, out=None):
+        """One token for each listed sequence, in order: (slots int64 [n],
+        copies as (src, dst) int64 arrays with -1 where there is none).  `out`
+        may pass those three arrays to fill (an engine reuses them every
+        step).  On a failure raises PagerError with `.done` = appends made."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        toks = np.ascontiguousarray(tokens, dtype=np.int32)
+        n = len(ids)
+        if len(toks) != n:
+            raise ValueError("one token per sequence")
+        if out is None:
+            slots, src, dst = (np.empty(n, dtype=np.int64) for _ in range(3))
+        else:
+            slots, src, dst = out
+            for a in out:
+                if a.dtype != np.int64 or a.shape != (n,) or not a.flags.c_contiguous:
+                    raise ValueError("out arrays must be contiguous int64 [n]")
+        done = ctypes.c_int64()
+        st = self._lib.pa_pager_append_batch(
+            self._h, _ptr(ids, ctypes.c_int64), _ptr(toks, ctypes.c_int32), n,
+            _ptr(slots, ctypes.c_int64), _ptr(src, ctypes.c_int64), _ptr(dst, ctypes.c_int64),
+            ctypes.byref(done))
+        if st != OK:
+            err = PagerError("pa_pager_append_batch", st)
+            err.done = done.value
+            raise err
+        return slots, (src, dst)
+
     def fork(self, parent: int, child: int) -> None:
         self._check("pa_pager_fork", self._lib.pa_pager_fork(self._h, parent, child))
 
     def free_sequence(self, seq_id: int) -> None:
         self._check("pa_pager_free_sequence", self._lib.pa_pager_free_sequence(self._h, seq_id))
 
-    def block_tables(self, seq_ids: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
-        """int32 [n][max_pages_per_seq] (padded with -1) and int32 [n]."""
+    def block_tables(self, seq_ids: Sequence[int], out=None) -> Tuple[np.ndarray, np.ndarray]:
+        """int32 [n][max_pages_per_seq] (padded with -1) and int32 [n]; `out`
+        may pass the (tables, lens) arrays to fill."""
         ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
-        tables = np.empty((len(ids), self.max_pages_per_seq), dtype=np.int32)
-        lens = np.empty(len(ids), dtype=np.int32)
+        n = len(ids)
+        if out is None:
+            tables = np.empty((n, self.max_pages_per_seq), dtype=np.int32)
+            lens = np.empty(n, dtype=np.int32)
+        else:
+            tables, lens = out
+            if (tables.dtype != np.int32 or tables.shape != (n, self.max_pages_per_seq) or
+                    lens.dtype != np.int32 or lens.shape != (n,) or
+                    not (tables.flags.c_contiguous and lens.flags.c_contiguous)):
+                raise ValueError("out arrays must be contiguous int32 [n][max_pages], [n]")
         self._check("pa_pager_block_tables", self._lib.pa_pager_block_tables(
             self._h, _ptr(ids, ctypes.c_int64), len(ids), _ptr(tables, ctypes.c_int32),
             _ptr(lens, ctypes.c_int32)))

@@ -241,3 +241,36 @@ def test_null_and_negative_arguments_are_rejected():
         assert not lib.pa_pager_create(8, 0, 4) and not lib.pa_pager_create(8, 16, 0)
     finally:
         lib.pa_pager_destroy(h)
+
+
+def test_append_batch_equals_appends_in_order():
+    rng = np.random.default_rng(21)
+    a = pa.Pager(40, 4, 10)
+    m = PagerModel(40, 4, 10)
+    for sid in range(6):
+        toks = rng.integers(0, 9, size=int(rng.integers(0, 14))).tolist()
+        a.add_sequence(sid, toks)
+        m.add_sequence(sid, toks)
+    a.fork(2, 6)
+    m.fork(2, 6)
+    for _ in range(12):
+        ids = rng.permutation(7)
+        toks = rng.integers(0, 9, size=7)
+        try:
+            slots, (src, dst) = a.append_batch(ids, toks)
+            done, status = 7, 0
+        except pgr.PagerError as e:
+            done, status = e.done, e.status
+            slots = src = dst = None
+        for i in range(7):
+            mst, mslot, mcopy = m.append(int(ids[i]), int(toks[i]))
+            if i < done:
+                assert mst == 0 and slots is not None
+                assert slots[i] == mslot
+                assert (None if src[i] < 0 else (src[i], dst[i])) == mcopy
+            else:
+                assert mst == status
+                break
+        assert a.stats() == m.stats()
+        if status:
+            break
