@@ -72,6 +72,9 @@ def parse_args():
                     help="split-KV partition in tokens (default: the workload's own)")
     ap.add_argument("--kernel", choices=["auto", "valu"], default="auto",
                     help="auto = pa_decode; valu = pa_decode_valu")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time the step as three calls (pa_reshape_and_cache, pa_decode, reduce) "
+                         "instead of pa_decode_append + reduce")
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured in a HIP graph (reported, not the value)")
@@ -213,15 +216,28 @@ def run_config(cid, args, headline):
         if flush_buf is not None:
             flush_buf.sum()  # read 1 GiB: evicts L2 and MALL, leaves no dirty lines
 
+    # The step's cache write runs inside the decode launch (pa_decode_append)
+    # unless --unfused or the vector kernel is asked for.
+    fused = args.kernel == "auto" and not args.unfused
+
     def step(ev=None, marks=True):
         """One step; `ev` = events to record, at the step's ends only or (marks)
         also between its kernels."""
         if ev:
             ev[0].record()
-        pa.pa_reshape_and_cache(new_key, new_value, k_cache, v_cache, new_slots)
-        if ev and marks:
-            ev[1].record()
-        if ps:
+        if not fused:
+            pa.pa_reshape_and_cache(new_key, new_value, k_cache, v_cache, new_slots)
+            if ev and marks:
+                ev[1].record()
+        elif ev and marks:
+            ev[1] = ev[0]
+        if fused and ps:
+            pa.pa_decode_append(None, query, new_key, new_value, new_slots, k_cache, v_cache,
+                                tables, lens, wl.scale, ps, po, pm, psum)
+        elif fused:
+            pa.pa_decode_append(out, query, new_key, new_value, new_slots, k_cache, v_cache,
+                                tables, lens, wl.scale)
+        elif ps:
             decode_fn(None, query, k_cache, v_cache, tables, lens, wl.scale, ps, po, pm, psum)
         else:
             decode_fn(out, query, k_cache, v_cache, tables, lens, wl.scale)
@@ -258,7 +274,7 @@ def run_config(cid, args, headline):
 
     step_ms = [e[0].elapsed_time(e[3]) for e in step_events]
     marked_step_ms = [e[0].elapsed_time(e[3]) for e in events]
-    cache_ms = [e[0].elapsed_time(e[1]) for e in events]
+    cache_ms = None if fused else [e[0].elapsed_time(e[1]) for e in events]
     decode_ms = [e[1].elapsed_time(e[2] if ps else e[3]) for e in events]
     reduce_ms = [e[2].elapsed_time(e[3]) for e in events] if ps else None
 
@@ -302,7 +318,8 @@ def run_config(cid, args, headline):
     t_step = float(np.mean(step_ms)) * 1e-3
     t_dec = float(np.mean(decode_ms)) * 1e-3
     gbs = nb["kv_unique"] / t_step / 1e9
-    achieved = nb["decode_kernel"] / t_dec / 1e9
+    launch_bytes = nb["decode_kernel"] + (nb["cache_write"] if fused else 0)
+    achieved = launch_bytes / t_dec / 1e9
     line = {
         "metric": METRIC,
         "value": round(gbs, 1),
@@ -319,15 +336,16 @@ def run_config(cid, args, headline):
         "config": {
             "workload": WORKLOAD_NAMES[cid],
             "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "page_size": P,
-            "partition_size": ps, "prefix_pages_shared": not args.unshared, "kernel": "pa_decode" if args.kernel == "auto" else
-            "pa_decode_valu", "cache_flush_between_steps": flush_buf is not None,
+            "partition_size": ps, "prefix_pages_shared": not args.unshared, "kernel": ("pa_decode_append (cache write inside the decode launch)" if fused else
+                       "pa_decode" if args.kernel == "auto" else "pa_decode_valu"), "cache_flush_between_steps": flush_buf is not None,
             "parallelism": "none (1 GPU)",
         },
         "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2),
         "seqs_per_s": round(B / t_step, 1),
         "effective_logical_kv_gbs": round(nb["kv_logical"] / t_step / 1e9, 1),
         "step_timing": "eager launches; HIP events on the library's stream at the step's ends",
-        "kernels_ms": {"cache_write": stats(cache_ms), "decode": stats(decode_ms),
+        "kernels_ms": {"cache_write": stats(cache_ms) if cache_ms else None,
+                       "decode": stats(decode_ms),
                        "reduce": stats(reduce_ms) if reduce_ms else None,
                        "step": stats(step_ms), "step_with_kernel_markers": stats(marked_step_ms)},
         "graph_step_ms": stats(graph_ms) if graph_ms else None,
@@ -343,7 +361,7 @@ def run_config(cid, args, headline):
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": read_traffic(cid, ps) if (wl.dtype == "bf16" and args.kernel == "auto")
             else None,
-            "algorithmic_bytes_per_launch": nb["decode_kernel"],
+            "algorithmic_bytes_per_launch": launch_bytes,
             "mean_launch_us": round(t_dec * 1e6, 2),
         },
     }

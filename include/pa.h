@@ -192,6 +192,33 @@ int pa_chunk_attention(void* out, const void* query, const void* k_cache, const 
                        int dtype, void* stream);
 
 /*
+ * pa_decode_append — one decode step in one call: write each sequence's new
+ * token into the pool, then attend over every cached token.
+ *
+ * The result (pool and outputs, bit for bit) equals pa_reshape_and_cache(key,
+ * value, k_cache, v_cache, slot_mapping, num_tokens = num_seqs, ...) followed
+ * by pa_decode(...) with the other arguments as given, provided every
+ * slot_mapping[b] is either negative (nothing written) or the slot of the
+ * sequence's last position, block_tables[b][(L_b - 1) / 16] * 16 +
+ * (L_b - 1) % 16 (the step that appends token L_b - 1 and attends over it;
+ * any other slot gives unspecified results).
+ *   key, value    [num_seqs][num_kv_heads][head_dim], dtype; key 16-byte aligned.
+ *   slot_mapping  [num_seqs] int64, device.
+ * For bf16 the write happens inside the decode launch: the work unit that
+ * reads a sequence's last page stores the new K row and V column first and
+ * then streams that page (one kernel instead of two).  fp32 runs the two
+ * kernels back to back.  Errors as for pa_decode, plus
+ * PA_ERR_INVALID_ARGUMENT for a NULL key, value or slot_mapping.
+ */
+int pa_decode_append(void* out, const void* query, const void* key, const void* value,
+                     const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                     const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                     int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                     int max_pages_per_seq, int64_t num_pages, float scale, int partition_size,
+                     int max_num_partitions, float* partial_out, float* partial_max,
+                     float* partial_sum, int dtype, void* stream);
+
+/*
  * pa_decode_valu — pa_decode with the vector-ALU kernel forced.
  *
  * Same arguments, layouts, results contract and errors as pa_decode.  For

@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     load,
     pa_chunk_attention,
     pa_decode,
+    pa_decode_append,
     pa_decode_reduce,
     pa_decode_valu,
     pa_export_pages,

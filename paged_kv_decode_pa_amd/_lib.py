@@ -36,6 +36,10 @@ _SIGNATURES = {
     "pa_decode_valu": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32,
                        _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _i32, _c_void_p,
                        _c_void_p, _c_void_p, _i32, _c_void_p],
+    "pa_decode_append": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                         _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32,
+                         _i64, _f32, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _i32,
+                         _c_void_p],
     "pa_chunk_attention": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                            _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
                            _f32, _i32, _c_void_p],
@@ -166,6 +170,38 @@ def pa_decode(out, query, k_cache, v_cache, block_tables, context_lens, scale,
     partial buffers are written (then call pa_decode_reduce)."""
     _decode("pa_decode", out, query, k_cache, v_cache, block_tables, context_lens, scale,
             partition_size, partial_out, partial_max, partial_sum, stream)
+
+
+def pa_decode_append(out, query, key, value, slot_mapping, k_cache, v_cache, block_tables,
+                     context_lens, scale, partition_size=0, partial_out=None, partial_max=None,
+                     partial_sum=None, stream=None) -> None:
+    """One decode step: write each sequence's new token (key/value [B][Hkv][D],
+    slot_mapping int64 [B]) and attend; see include/pa.h."""
+    B, Hq, D = query.shape
+    Hkv = k_cache.shape[1]
+    if key.shape != (B, Hkv, D) or value.shape != key.shape or tuple(slot_mapping.shape) != (B,):
+        raise ValueError("key, value and slot_mapping must hold one token per sequence")
+    if not (key.dtype == value.dtype == query.dtype == k_cache.dtype):
+        raise TypeError("key, value, query and pools must share one dtype")
+    if k_cache.shape[2:] != (PAGE_SIZE, D) or v_cache.shape[1:] != (Hkv, D, PAGE_SIZE):
+        raise ValueError("pool shape does not match query")
+    if block_tables.shape[0] != B or tuple(context_lens.shape) != (B,):
+        raise ValueError("block_tables / context_lens do not match the batch")
+    max_parts = 0
+    if partition_size:
+        max_parts = partial_max.shape[2]
+        if (partial_out.shape != (B, Hq, max_parts, D) or partial_max.shape != (B, Hq, max_parts)
+                or partial_sum.shape != (B, Hq, max_parts)):
+            raise ValueError("partial buffers have the wrong shape")
+    elif out is None or out.shape != query.shape or out.dtype != query.dtype:
+        raise ValueError("out must match query")
+    lib = load()
+    _check("pa_decode_append", lib.pa_decode_append(
+        _ptr(out), _ptr(query), _ptr(key), _ptr(value), _ptr(slot_mapping), _ptr(k_cache),
+        _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, D, PAGE_SIZE,
+        block_tables.shape[1], k_cache.shape[0], float(scale), int(partition_size), max_parts,
+        _ptr(partial_out), _ptr(partial_max), _ptr(partial_sum), _dtype_code(query),
+        _stream(stream)))
 
 
 def pa_chunk_attention(out, query, k_cache, v_cache, block_tables, context_lens, query_start,

@@ -141,6 +141,40 @@ struct WaveAttn {
   }
 };
 
+// The step's new token of sequence `seq` (bf16): its K row and V column for
+// kv head `kvh`, requested with the unit's other first loads and stored into
+// its pool slot by the wave that reads the sequence's last page, before that
+// page's tile is loaded.  Same wave, same addresses, program order: the tile
+// load sees the stored bits.  Lane l < D/8 moves the K row's 16-byte chunk l,
+// every lane moves V dims l, l + 64.
+template <int D>
+struct NewToken {
+  u32x4 k;
+  uint16_t v[D / 64];
+  int64_t slot;
+  __device__ void request(const DecodeParams& p, int seq, int kvh, int lane) {
+    slot = p.new_slots[seq];
+    const size_t row = (size_t(seq) * p.num_kv_heads + kvh) * D;
+    const uint16_t* kr = static_cast<const uint16_t*>(p.new_key) + row;
+    const uint16_t* vr = static_cast<const uint16_t*>(p.new_value) + row;
+    k = u32x4{0u, 0u, 0u, 0u};
+    if (lane < D / 8) k = *reinterpret_cast<const u32x4*>(kr + 8 * lane);
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) v[i] = vr[lane + 64 * i];
+  }
+  __device__ void store(const DecodeParams& p, int kvh, int lane) const {
+    if (slot < 0 || slot >= p.num_pages * kPage) return;
+    const int64_t page = slot / kPage;
+    const int off = int(slot % kPage);
+    const size_t tile = (size_t(page) * p.num_kv_heads + kvh) * kPage * D;
+    uint16_t* kt = static_cast<uint16_t*>(const_cast<void*>(p.k_cache)) + tile + size_t(off) * D;
+    uint16_t* vt = static_cast<uint16_t*>(const_cast<void*>(p.v_cache)) + tile;
+    if (lane < D / 8) *reinterpret_cast<u32x4*>(kt + 8 * lane) = k;
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) vt[(lane + 64 * i) * kPage + off] = v[i];
+  }
+};
+
 template <int D>
 __device__ inline PageStream<D> make_stream(const DecodeParams& p, int seq, int kvh, int first,
                                             int step, int row_end, int lane) {
@@ -244,7 +278,8 @@ struct FirstPages {
 // first and no wave is spent on a partition past a context's end.  Returns
 // false for an index past the last unit.  NC * 64 >= batch.
 template <int NC>
-__device__ bool split_unit(const DecodeParams& p, int useq, int lane, int& seq, int& part) {
+__device__ bool split_unit(const DecodeParams& p, int useq, int lane, int& seq, int& part,
+                           int& seq_pages) {
   const int PP = p.pages_per_partition;
   int pages[NC], nfull[NC], hasp[NC];
   load_pages<NC>(p, lane, pages);
@@ -296,6 +331,10 @@ __device__ bool split_unit(const DecodeParams& p, int useq, int lane, int& seq, 
     }
   }
   seq = __builtin_amdgcn_readfirstlane(seq);
+  seq_pages = 0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    if (c == (seq >> 6)) seq_pages = __builtin_amdgcn_readlane(pages[c], seq & 63);
   return seq >= 0;
 }
 
@@ -338,9 +377,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   const int r = lane & 15, j = lane >> 4;
   const int G = p.group;
 
-  int seq, part;
+  int seq, part, seq_pages = 0;
   if constexpr (NC > 0) {
-    if (!split_unit<NC>(p, useq, lane, seq, part)) return;
+    if (!split_unit<NC>(p, useq, lane, seq, part, seq_pages)) return;
   } else {
     seq = useq % p.num_seqs;  // plain grid: partitions past a context exit below
     part = useq / p.num_seqs;
@@ -348,8 +387,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   seq = __builtin_amdgcn_readfirstlane(seq);
   part = __builtin_amdgcn_readfirstlane(part);
 
-  // Issued together before any of them returns: the sharing test, length,
-  // page ids, query.
+  // Issued together before any of them returns: the new token (when this
+  // partition holds the sequence's last page and the launch appends), the
+  // sharing test, length, page ids, query.
+  const bool appends = p.new_key != nullptr;
+  bool writes = false;
+  NewToken<D> nt;
+  if constexpr (NC > 0) {
+    writes = appends && (part + 1) * p.pages_per_partition >= seq_pages;
+    if (writes) nt.request(p, seq, kvh, lane);
+  }
   SharingTest<NC> sharing;
   sharing.request(p, lane);
   const int lo = part * p.pages_per_partition;
@@ -364,6 +411,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   if (n > p.max_pages_per_seq) n = p.max_pages_per_seq;
   const int hi = min(lo + p.pages_per_partition, n);
   if (lo >= hi) return;  // partition past the context: nothing to write
+  if constexpr (NC == 0) {  // the plain grid learns the length only now
+    writes = appends && hi == n;
+    if (writes) nt.request(p, seq, kvh, lane);
+  }
+  if (writes) nt.store(p, kvh, lane);
   ps.count = hi - lo;
   wa.run(ps, lo, L, lane, sharing.shared(p, seq, lane));
 
@@ -395,6 +447,11 @@ __global__ __launch_bounds__(kBlock) void decode_whole_kernel(DecodeParams p) {
   const int r = lane & 15, j = lane >> 4;
   const int G = p.group;
 
+  // Every wave requests the new token with its first loads (the length, which
+  // says which wave reads the last page, is not known yet).
+  const bool appends = p.new_key != nullptr;
+  NewToken<D> nt;
+  if (appends) nt.request(p, seq, kvh, lane);
   PageStream<D> ps = make_stream<D>(p, seq, kvh, w, kWaves, p.max_pages_per_seq, lane);
   const int L = p.context_lens[seq];
   WaveAttn<D> wa;
@@ -406,6 +463,7 @@ __global__ __launch_bounds__(kBlock) void decode_whole_kernel(DecodeParams p) {
     store_zeros<uint16_t, D>(p, seq, kvh);
     return;
   }
+  if (appends && (hi - 1) % kWaves == w) nt.store(p, kvh, lane);
   ps.count = w < hi ? (hi - w + kWaves - 1) / kWaves : 0;
   // Cached loads throughout: with four waves per unit this kernel runs far
   // fewer waves than the split one, and the nontemporal hint measured up to

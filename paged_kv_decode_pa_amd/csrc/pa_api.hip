@@ -39,12 +39,16 @@ int check_common(int head_dim, int page_size, int dtype) {
 
 enum class DecodeKernel { kAuto, kValu };
 
+// new_key == NULL: decode only.  Otherwise the launch first writes each
+// sequence's new token (new_key/new_value rows, slot new_slots[b]): inside the
+// matrix-core kernels, or as a separate cache-write launch for the others.
 int decode_impl(DecodeKernel which, void* out, const void* query, const void* k_cache,
                 const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
                 int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int page_size,
                 int max_pages_per_seq, int64_t num_pages, float scale, int partition_size,
                 int max_num_partitions, float* partial_out, float* partial_max,
-                float* partial_sum, int dtype, void* stream) {
+                float* partial_sum, int dtype, void* stream, const void* new_key = nullptr,
+                const void* new_value = nullptr, const int64_t* new_slots = nullptr) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_pages_per_seq <= 0 ||
       num_pages <= 0 || partition_size < 0)
     return PA_ERR_INVALID_ARGUMENT;
@@ -57,6 +61,7 @@ int decode_impl(DecodeKernel which, void* out, const void* query, const void* k_
   if (!aligned16(query) || !aligned16(k_cache) || !aligned16(v_cache))
     return PA_ERR_INVALID_ARGUMENT;
   if (!isfinite(scale)) return PA_ERR_INVALID_ARGUMENT;
+  if (new_key && (!new_value || !new_slots || !aligned16(new_key))) return PA_ERR_INVALID_ARGUMENT;
   const bool split = partition_size > 0;
   if (split) {
     if (partition_size % PA_PAGE_SIZE != 0 || max_num_partitions < 1) return PA_ERR_INVALID_ARGUMENT;
@@ -90,11 +95,25 @@ int decode_impl(DecodeKernel which, void* out, const void* query, const void* k_
   p.pages_per_partition = split ? partition_size / PA_PAGE_SIZE : 0;
   p.num_partitions = int(parts);
   p.num_units = int(units);
+  p.new_key = nullptr;
+  p.new_value = nullptr;
+  p.new_slots = nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = dtype == PA_DTYPE_BF16;
-  const hipError_t err = (bf16 && which == DecodeKernel::kAuto)
-                             ? pa::launch_decode_mfma(p, head_dim, s)
-                             : pa::launch_decode_valu(p, head_dim, bf16, s);
+  const bool mfma = bf16 && which == DecodeKernel::kAuto;
+  if (new_key && mfma) {
+    p.new_key = new_key;
+    p.new_value = new_value;
+    p.new_slots = new_slots;
+  } else if (new_key) {
+    const hipError_t e = pa::launch_reshape_and_cache(new_key, new_value, const_cast<void*>(k_cache),
+                                                      const_cast<void*>(v_cache), new_slots,
+                                                      num_seqs, num_kv_heads, head_dim, num_pages,
+                                                      bf16, s);
+    if (e != hipSuccess) return PA_ERR_LAUNCH;
+  }
+  const hipError_t err = mfma ? pa::launch_decode_mfma(p, head_dim, s)
+                              : pa::launch_decode_valu(p, head_dim, bf16, s);
   return err == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
@@ -148,6 +167,21 @@ int pa_decode(void* out, const void* query, const void* k_cache, const void* v_c
                      context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
                      max_pages_per_seq, num_pages, scale, partition_size, max_num_partitions,
                      partial_out, partial_max, partial_sum, dtype, stream);
+}
+
+int pa_decode_append(void* out, const void* query, const void* key, const void* value,
+                     const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                     const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                     int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                     int max_pages_per_seq, int64_t num_pages, float scale, int partition_size,
+                     int max_num_partitions, float* partial_out, float* partial_max,
+                     float* partial_sum, int dtype, void* stream) {
+  if (!key) return PA_ERR_INVALID_ARGUMENT;
+  return decode_impl(DecodeKernel::kAuto, out, query, k_cache, v_cache, block_tables,
+                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
+                     max_pages_per_seq, num_pages, scale, partition_size, max_num_partitions,
+                     partial_out, partial_max, partial_sum, dtype, stream, key, value,
+                     slot_mapping);
 }
 
 int pa_chunk_attention(void* out, const void* query, const void* k_cache, const void* v_cache,

@@ -34,6 +34,11 @@ struct DecodeParams {
   int pages_per_partition;  // 0: the whole context is one unit
   int num_partitions;       // partitions per (sequence, kv head) in the grid
   int num_units;            // num_seqs * num_partitions * num_kv_heads
+  // The step's appended token per sequence, written by the decode launch
+  // itself (NULL new_key: the caller wrote it with pa_reshape_and_cache).
+  const void* new_key;      // [num_seqs][num_kv_heads][head_dim]
+  const void* new_value;    // [num_seqs][num_kv_heads][head_dim]
+  const int64_t* new_slots; // [num_seqs]; < 0 writes nothing
 };
 
 // Multi-token causal attention over the same cache: sequence b's new query
