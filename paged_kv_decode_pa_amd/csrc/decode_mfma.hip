@@ -30,6 +30,60 @@ namespace {
 
 constexpr float kRescaleSlack = 8.0f;   // base 2: P may reach 2^8 before a rescale
 
+// The step's new token of sequence `seq` (bf16): its K row and V column for
+// kv head `kvh`, requested with the unit's first loads.  The wave that reads
+// the sequence's last page puts the token into that page's tile registers
+// (patch), so the tile need not wait for the pool, and stores it into the pool
+// slot after its stream (store).  Lane l < D/8 holds the K row's 16-byte chunk
+// l; every lane holds V dims l and l + 64.
+template <int D>
+struct NewToken {
+  u32x4 k;
+  uint16_t v[D / 64];
+  int64_t slot;
+  __device__ void request(const DecodeParams& p, int seq, int kvh, int lane) {
+    slot = p.new_slots[seq];
+    const size_t row = (size_t(seq) * p.num_kv_heads + kvh) * D;
+    const uint16_t* kr = static_cast<const uint16_t*>(p.new_key) + row;
+    const uint16_t* vr = static_cast<const uint16_t*>(p.new_value) + row;
+    k = u32x4{0u, 0u, 0u, 0u};
+    if (lane < D / 8) k = *reinterpret_cast<const u32x4*>(kr + 8 * lane);
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) v[i] = vr[lane + 64 * i];
+  }
+  __device__ bool valid(const DecodeParams& p) const {
+    return slot >= 0 && slot < p.num_pages * kPage;
+  }
+  // Overwrite in-page slot s of a page tile with this token (tile layouts as
+  // in PageTile: lane (r, j) holds K row r's chunks 4kb + j and V^T rows
+  // 16db + r at tokens 4j .. 4j + 3).
+  __device__ void patch(PageTile<D>& t, int s, int lane) const {
+    const int r = lane & 15, j = lane >> 4;
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb) {
+      u32x4 x;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) x[c] = __shfl(k[c], 4 * kb + j);
+      if (r == s) t.k[kb] = __builtin_bit_cast(bf16x8, x);
+    }
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      const int x = __shfl(int(v[db / 4]), 16 * (db % 4) + r);
+      if (j == s / 4) t.v[db][s % 4] = short(x);
+    }
+  }
+  __device__ void store(const DecodeParams& p, int kvh, int lane) const {
+    const int64_t page = slot / kPage;
+    const int off = int(slot % kPage);
+    const size_t tile = (size_t(page) * p.num_kv_heads + kvh) * kPage * D;
+    uint16_t* kt = static_cast<uint16_t*>(const_cast<void*>(p.k_cache)) + tile + size_t(off) * D;
+    uint16_t* vt = static_cast<uint16_t*>(const_cast<void*>(p.v_cache)) + tile;
+    if (lane < D / 8) *reinterpret_cast<u32x4*>(kt + 8 * lane) = k;
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) vt[(lane + 64 * i) * kPage + off] = v[i];
+  }
+};
+
 // One wave's online-softmax attention state for one kv head's query group.
 template <int D>
 struct WaveAttn {
@@ -106,10 +160,15 @@ struct WaveAttn {
   // would go back to HBM under the nontemporal hint); the last one to three
   // pages are finished after it.  Only a one-page stream requests a tile
   // twice (its clamped second request).
+  // With `append`, the stream's last page is the sequence's last page and
+  // the step's new token `nt` goes into its tile (in-page slot (L-1) % 16)
+  // before it is computed.
   template <bool Stream>
-  __device__ void walk(PageStream<D>& ps, int page0, int L, int lane) {
+  __device__ void walk(PageStream<D>& ps, int page0, int L, int lane, bool append,
+                       const NewToken<D>& nt) {
     const int n = ps.count;
     auto valid = [&](int k) { return L - (page0 + ps.step * k) * kPage; };
+    const int s = (L - 1) % kPage;
     PageTile<D> ta, tb;
     bool ok_a = ps.template issue<Stream>(ta, 0, lane);
     bool ok_b = ps.template issue<Stream>(tb, 1, lane);  // a one-page stream repeats tile 0
@@ -121,10 +180,13 @@ struct WaveAttn {
       ok_b = ps.template issue<Stream>(tb, k + 3, lane);
     }
     const int rem = n - k;  // 1 (only when n == 1), 2 or 3 pages left
+    if (append && rem == 1) nt.patch(ta, s, lane);
     if (ok_a) page(ta, valid(k));
     if (rem >= 2) {
       const bool ok_c = rem == 3 && ps.template issue<Stream>(ta, k + 2, lane);
+      if (append && rem == 2) nt.patch(tb, s, lane);
       if (ok_b) page(tb, valid(k + 1));
+      if (append && rem == 3) nt.patch(ta, s, lane);
       if (ok_c) page(ta, valid(k + 2));
     }
   }
@@ -132,46 +194,13 @@ struct WaveAttn {
   // sequence (cached loads); otherwise the pages stream with the nontemporal
   // hint.  Its loads were issued with the page ids, which the first tile
   // needs anyway, so deciding first costs no extra round trip.
-  __device__ void run(PageStream<D>& ps, int page0, int L, int lane, bool shared) {
+  __device__ void run(PageStream<D>& ps, int page0, int L, int lane, bool shared,
+                      bool append, const NewToken<D>& nt) {
     if (ps.count <= 0) return;
     if (shared)
-      walk<false>(ps, page0, L, lane);
+      walk<false>(ps, page0, L, lane, append, nt);
     else
-      walk<true>(ps, page0, L, lane);
-  }
-};
-
-// The step's new token of sequence `seq` (bf16): its K row and V column for
-// kv head `kvh`, requested with the unit's other first loads and stored into
-// its pool slot by the wave that reads the sequence's last page, before that
-// page's tile is loaded.  Same wave, same addresses, program order: the tile
-// load sees the stored bits.  Lane l < D/8 moves the K row's 16-byte chunk l,
-// every lane moves V dims l, l + 64.
-template <int D>
-struct NewToken {
-  u32x4 k;
-  uint16_t v[D / 64];
-  int64_t slot;
-  __device__ void request(const DecodeParams& p, int seq, int kvh, int lane) {
-    slot = p.new_slots[seq];
-    const size_t row = (size_t(seq) * p.num_kv_heads + kvh) * D;
-    const uint16_t* kr = static_cast<const uint16_t*>(p.new_key) + row;
-    const uint16_t* vr = static_cast<const uint16_t*>(p.new_value) + row;
-    k = u32x4{0u, 0u, 0u, 0u};
-    if (lane < D / 8) k = *reinterpret_cast<const u32x4*>(kr + 8 * lane);
-#pragma unroll
-    for (int i = 0; i < D / 64; ++i) v[i] = vr[lane + 64 * i];
-  }
-  __device__ void store(const DecodeParams& p, int kvh, int lane) const {
-    if (slot < 0 || slot >= p.num_pages * kPage) return;
-    const int64_t page = slot / kPage;
-    const int off = int(slot % kPage);
-    const size_t tile = (size_t(page) * p.num_kv_heads + kvh) * kPage * D;
-    uint16_t* kt = static_cast<uint16_t*>(const_cast<void*>(p.k_cache)) + tile + size_t(off) * D;
-    uint16_t* vt = static_cast<uint16_t*>(const_cast<void*>(p.v_cache)) + tile;
-    if (lane < D / 8) *reinterpret_cast<u32x4*>(kt + 8 * lane) = k;
-#pragma unroll
-    for (int i = 0; i < D / 64; ++i) vt[(lane + 64 * i) * kPage + off] = v[i];
+      walk<true>(ps, page0, L, lane, append, nt);
   }
 };
 
@@ -415,9 +444,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
     writes = appends && hi == n;
     if (writes) nt.request(p, seq, kvh, lane);
   }
-  if (writes) nt.store(p, kvh, lane);
+  writes = writes && nt.valid(p);
   ps.count = hi - lo;
-  wa.run(ps, lo, L, lane, sharing.shared(p, seq, lane));
+  wa.run(ps, lo, L, lane, sharing.shared(p, seq, lane), writes, nt);
+  if (writes) nt.store(p, kvh, lane);
 
   // Partial of this partition: o = acc / l, m in natural-log units, l.
   const float l = __shfl(wa.acc[D / 16][0], r);  // row 0 of the denominator block
@@ -463,12 +493,13 @@ __global__ __launch_bounds__(kBlock) void decode_whole_kernel(DecodeParams p) {
     store_zeros<uint16_t, D>(p, seq, kvh);
     return;
   }
-  if (appends && (hi - 1) % kWaves == w) nt.store(p, kvh, lane);
+  const bool writes = appends && (hi - 1) % kWaves == w && nt.valid(p);
   ps.count = w < hi ? (hi - w + kWaves - 1) / kWaves : 0;
   // Cached loads throughout: with four waves per unit this kernel runs far
   // fewer waves than the split one, and the nontemporal hint measured up to
   // 25% slower here (long contexts of the 256-sequence batch).
-  wa.run(ps, w, L, lane, /*shared=*/true);
+  wa.run(ps, w, L, lane, /*shared=*/true, writes, nt);
+  if (writes) nt.store(p, kvh, lane);
 
   MergeLds lds(smem);
   if (r < G) {
