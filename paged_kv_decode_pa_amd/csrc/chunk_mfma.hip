@@ -53,16 +53,22 @@ struct ColumnAttn {
     for (int db = 0; db <= D / 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Scores of the page starting at token `base`, base 2, with the causal
-  // mask (which also masks positions past the context).
+  // Scores of the page starting at token `base`, base 2.  Masked: with the
+  // causal mask (which also masks positions past the context); otherwise
+  // every token of the page precedes every real column's position.
+  template <bool Masked>
   __device__ void scores(const PageTile<D>& t, int base, float (&s2)[4]) const {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < D / 32; ++kb)
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[kb], qop[kb], s, 0, 0, 0);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      s2[e] = base + 4 * j + e > pos ? -INFINITY : s[e] * scale_log2;
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (Masked)
+        s2[e] = base + 4 * j + e > pos ? -INFINITY : s[e] * scale_log2;
+      else
+        s2[e] = s[e] * scale_log2;
+    }
   }
 
   // Online-softmax update with the page's scores, given whether any lane's
@@ -70,6 +76,9 @@ struct ColumnAttn {
   // A column may have no unmasked token on a page (its position precedes the
   // page): its P is then 0, and while its reference is still -inf the
   // rescale factor is 0, so no 0 * inf or inf - inf arises.
+  // Unmasked, every column has 16 finite scores, so after the rescale its
+  // reference is finite and no select is needed.
+  template <bool Masked>
   __device__ void accumulate(const PageTile<D>& t, const float (&s2)[4], float lm, bool raise) {
     if (raise) {
       float pm = fmaxf(lm, __shfl_xor(lm, 16));
@@ -82,10 +91,13 @@ struct ColumnAttn {
     }
     s16x4 pb;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      pb[e] = s2[e] == -INFINITY
-                  ? short(0)
-                  : static_cast<short>(f32_to_bf16(__builtin_amdgcn_exp2f(s2[e] - m_run)));
+    for (int e = 0; e < 4; ++e) {
+      const short p = static_cast<short>(f32_to_bf16(__builtin_amdgcn_exp2f(s2[e] - m_run)));
+      if constexpr (Masked)
+        pb[e] = s2[e] == -INFINITY ? short(0) : p;
+      else
+        pb[e] = p;
+    }
 #pragma unroll
     for (int db = 0; db < D / 16; ++db)
       acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[db], pb, acc[db], 0, 0, 0);
@@ -109,57 +121,71 @@ __device__ inline void zero_past(PageTile<D>& t, int valid, int j) {
 // the reads of its result, the compiler was seen to let a taken branch reach
 // the reads fewer wait states after the instruction than the result needs
 // (wrong, run-to-run varying scores).
-template <int D, int NB>
+template <int D, int NB, bool Masked>
 __device__ inline void page_blocks(ColumnAttn<D> (&wa)[NB], const PageTile<D>& t, int base) {
   float s2[NB][4];
   float lm[NB];
   bool raise[NB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) wa[nb].scores(t, base, s2[nb]);
+  for (int nb = 0; nb < NB; ++nb) wa[nb].template scores<Masked>(t, base, s2[nb]);
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     lm[nb] = fmaxf(fmaxf(s2[nb][0], s2[nb][1]), fmaxf(s2[nb][2], s2[nb][3]));
     raise[nb] = __ballot(lm[nb] > wa[nb].m_run + kSlack) != 0;
   }
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) wa[nb].accumulate(t, s2[nb], lm[nb], raise[nb]);
+  for (int nb = 0; nb < NB; ++nb) wa[nb].template accumulate<Masked>(t, s2[nb], lm[nb], raise[nb]);
 }
 
 // Two tiles in ping-pong, as in the decode kernel; ordinal k is page
-// page0 + step * k.  The loop stops three ordinals before the end, so the
-// pages it computes are all full (only the sequence's last page can be
-// partial); the last one to three are zeroed past the context first.
+// page0 + step * k.  The first loop runs while both pages of a step lie
+// wholly before `visible_end` (every real column of the wave sees all their
+// tokens): far from the diagonal, which is most pages of a long context, the
+// step skips the causal mask and its selects.  One loop per variant keeps a
+// single copy of the page step in each loop body.  The loops stop three
+// ordinals before the end, so the pages they compute are all full (only the
+// sequence's last page can be partial); the last one to three are zeroed
+// past the context first.
 template <int D, int NB>
 __device__ inline void run_blocks(ColumnAttn<D> (&wa)[NB], PageStream<D>& ps, int page0, int L,
-                                  int lane) {
+                                  int visible_end, int lane) {
   const int n = ps.count;
   if (n <= 0) return;
   const int j = lane >> 4;
   auto base = [&](int k) { return (page0 + ps.step * k) * kPage; };
+  // Ordinals below n_clear hold pages wholly before visible_end.
+  const int last_clear = visible_end / kPage - 1;  // last page index wholly visible
+  const int n_clear = last_clear < page0 ? 0 : (last_clear - page0) / ps.step + 1;
   PageTile<D> ta, tb;
   bool ok_a = ps.template issue<false>(ta, 0, lane);
   bool ok_b = ps.template issue<false>(tb, 1, lane);
   int k = 0;
-  for (; k + 3 < n; k += 2) {
-    if (ok_a) page_blocks<D, NB>(wa, ta, base(k));
+  for (; k + 3 < n && k + 1 < n_clear; k += 2) {
+    if (ok_a) page_blocks<D, NB, false>(wa, ta, base(k));
     ok_a = ps.template issue<false>(ta, k + 2, lane);
-    if (ok_b) page_blocks<D, NB>(wa, tb, base(k + 1));
+    if (ok_b) page_blocks<D, NB, false>(wa, tb, base(k + 1));
+    ok_b = ps.template issue<false>(tb, k + 3, lane);
+  }
+  for (; k + 3 < n; k += 2) {
+    if (ok_a) page_blocks<D, NB, true>(wa, ta, base(k));
+    ok_a = ps.template issue<false>(ta, k + 2, lane);
+    if (ok_b) page_blocks<D, NB, true>(wa, tb, base(k + 1));
     ok_b = ps.template issue<false>(tb, k + 3, lane);
   }
   const int rem = n - k;
   if (ok_a) {
     zero_past(ta, L - base(k), j);
-    page_blocks<D, NB>(wa, ta, base(k));
+    page_blocks<D, NB, true>(wa, ta, base(k));
   }
   if (rem >= 2) {
     const bool ok_c = rem == 3 && ps.template issue<false>(ta, k + 2, lane);
     if (ok_b) {
       zero_past(tb, L - base(k + 1), j);
-      page_blocks<D, NB>(wa, tb, base(k + 1));
+      page_blocks<D, NB, true>(wa, tb, base(k + 1));
     }
     if (ok_c) {
       zero_past(ta, L - base(k + 2), j);
-      page_blocks<D, NB>(wa, ta, base(k + 2));
+      page_blocks<D, NB, true>(wa, ta, base(k + 2));
     }
   }
 }
@@ -221,7 +247,10 @@ __global__ __launch_bounds__(kBlock) void chunk_attention_kernel(ChunkParams p) 
     // position of the column's token (< 0 only if q_len exceeds the context)
     wa[nb].init(qrow, real, r, j, real ? L - q_len + i : -1, p.scale_log2);
   }
-  run_blocks<D, NB>(wa, ps, w, L, lane);
+  // Tokens below visible_end are seen by every real column of the group (the
+  // first column's token sits at the smallest position).
+  const int visible_end = L - q_len + c0 / G + 1;
+  run_blocks<D, NB>(wa, ps, w, L, visible_end, lane);
 
   // Merge the four waves per column (fixed wave order) and store the rows,
   // one block at a time through the same LDS.
