@@ -72,6 +72,9 @@ def parse_args():
                     help="split-KV partition in tokens (default: the workload's own)")
     ap.add_argument("--kernel", choices=["auto", "valu"], default="auto",
                     help="auto = pa_decode; valu = pa_decode_valu")
+    ap.add_argument("--cascade", action="store_true",
+                    help="read pages shared by a group of sequences once per group "
+                         "(pa_decode_cascade; split-KV only)")
     ap.add_argument("--unfused", action="store_true",
                     help="time the step as three calls (pa_reshape_and_cache, pa_decode, reduce) "
                          "instead of pa_decode_append + reduce")
@@ -219,6 +222,17 @@ def run_config(cid, args, headline):
     # The step's cache write runs inside the decode launch (pa_decode_append)
     # unless --unfused or the vector kernel is asked for.
     fused = args.kernel == "auto" and not args.unfused
+    groups = None
+    if args.cascade:
+        if not ps or wl.dtype != "bf16" or args.kernel != "auto":
+            raise SystemExit("--cascade needs a bf16 workload, the matrix-core kernels and a "
+                             "partition size")
+        t0 = time.perf_counter()
+        g = pa.prefix_groups(wl.block_tables, wl.context_lens, ps // P)
+        plan_us = (time.perf_counter() - t0) * 1e6
+        groups = dict(g)
+        for k in ("group_start", "group_seqs", "group_partitions", "seq_first_partition"):
+            groups[k] = torch.from_numpy(np.ascontiguousarray(g[k], dtype=np.int32)).to(dev)
 
     def step(ev=None, marks=True):
         """One step; `ev` = events to record, at the step's ends only or (marks)
@@ -231,7 +245,11 @@ def run_config(cid, args, headline):
                 ev[1].record()
         elif ev and marks:
             ev[1] = ev[0]
-        if fused and ps:
+        if groups is not None:
+            pa.pa_decode_cascade(query, k_cache, v_cache, tables, lens, wl.scale, ps, po, pm,
+                                 psum, groups, **({"key": new_key, "value": new_value,
+                                                   "slot_mapping": new_slots} if fused else {}))
+        elif fused and ps:
             pa.pa_decode_append(None, query, new_key, new_value, new_slots, k_cache, v_cache,
                                 tables, lens, wl.scale, ps, po, pm, psum)
         elif fused:
@@ -339,6 +357,11 @@ def run_config(cid, args, headline):
             "partition_size": ps, "prefix_pages_shared": not args.unshared, "kernel": ("pa_decode_append (cache write inside the decode launch)" if fused else
                        "pa_decode" if args.kernel == "auto" else "pa_decode_valu"), "cache_flush_between_steps": flush_buf is not None,
             "parallelism": "none (1 GPU)",
+            "shared_prefix_groups": (None if groups is None else
+                                     {"groups": int(groups["num_groups"]),
+                                      "max_members": int(groups["max_group_size"]),
+                                      "shared_partitions": int(groups["max_group_partitions"]),
+                                      "host_plan_us": round(plan_us, 1)}),
         },
         "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2),
         "seqs_per_s": round(B / t_step, 1),

@@ -219,6 +219,50 @@ int pa_decode_append(void* out, const void* query, const void* key, const void* 
                      float* partial_sum, int dtype, void* stream);
 
 /*
+ * pa_decode_cascade — split-KV decode that reads pages shared by a group of
+ * sequences once per group (prefix reuse: llm-d blog post, prefix-cache
+ * sections; requests with a common prompt prefix point at the same pages).
+ *
+ * Group g's members are group_seqs[group_start[g] .. group_start[g + 1]) (batch
+ * indices).  They hold the same physical page ids in block-table columns
+ * 0 .. group_partitions[g] * (partition_size / 16) - 1, and every token of
+ * those pages lies inside every member's context.  For each such partition and
+ * kv head one work unit reads the pages once and computes every member's
+ * partial for it: the members' query heads are the columns of the matrix
+ * tiles, up to 64 per wave.  Then the ordinary split-KV kernel computes each
+ * sequence's partitions from seq_first_partition[b] on (0 for sequences in no
+ * group).  With key/value/slot_mapping non-NULL it also writes the step's new
+ * token first, as pa_decode_append does.  The partial arrays end up as
+ * pa_decode (split) writes them: merge them with pa_decode_reduce.
+ *
+ *   num_groups, max_group_size, max_group_partitions  host bounds that size
+ *               the grid: groups of more members or partitions are not fully
+ *               computed (unspecified results).  max_group_partitions must
+ *               not exceed max_num_partitions.
+ *   group_start [num_groups + 1], group_seqs, group_partitions [num_groups],
+ *   seq_first_partition [num_seqs]: int32, device.  seq_first_partition[b]
+ *               must equal group_partitions of b's group (0 outside groups).
+ *   Other arguments as for pa_decode with partition_size > 0.
+ * Results match pa_decode (split) to rounding.  The shared partitions'
+ * partials sum their pages in another order, so bits differ, but they are
+ * deterministic.  Members outside [0, num_seqs) are skipped.  bf16 only:
+ * other dtypes return PA_ERR_UNSUPPORTED.  num_groups == 0 is pa_decode (or
+ * pa_decode_append).  Host-checkable errors as for pa_decode, plus
+ * PA_ERR_INVALID_ARGUMENT for partition_size 0, NULL group arrays with
+ * num_groups > 0, or key/value/slot_mapping given only in part.
+ */
+int pa_decode_cascade(const void* query, const void* key, const void* value,
+                      const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                      int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                      int max_pages_per_seq, int64_t num_pages, float scale, int partition_size,
+                      int max_num_partitions, float* partial_out, float* partial_max,
+                      float* partial_sum, int num_groups, int max_group_size,
+                      int max_group_partitions, const int32_t* group_start,
+                      const int32_t* group_seqs, const int32_t* group_partitions,
+                      const int32_t* seq_first_partition, int dtype, void* stream);
+
+/*
  * pa_decode_valu — pa_decode with the vector-ALU kernel forced.
  *
  * Same arguments, layouts, results contract and errors as pa_decode.  For

@@ -127,6 +127,26 @@ int pa_pager_get_stats(const pa_pager* pager, pa_pager_stats* out);
 int pa_pager_drain_events(pa_pager* pager, int32_t* kinds, int64_t* pages, uint64_t* hashes,
                           int64_t capacity, int64_t* count);
 
+/* Groups of sequences that share their first pages, in the form
+ * pa_decode_cascade (pa.h) takes.  block_tables [num_seqs][max_pages_per_seq]
+ * and context_lens [num_seqs] are host int32 arrays (the rows a batch's
+ * decode reads).  Sequences are grouped when they hold the same page id in
+ * column 0.  A group's shared prefix is the longest run of columns from 0 in
+ * which every member holds the first member's page id, counting only pages
+ * that lie wholly before each member's last token (so the page that receives
+ * the step's token is never in it), in whole partitions of
+ * pages_per_partition pages.  Groups of one member or of no whole partition
+ * are dropped.  Groups are ordered by their first member and members by batch
+ * index.  Outputs (host; sized for the worst case): group_start [num_seqs +
+ * 1], group_seqs [num_seqs], group_partitions [num_seqs], seq_first_partition
+ * [num_seqs] (0 outside groups); *num_groups, *max_group_size and
+ * *max_group_partitions. */
+int pa_pager_prefix_groups(const int32_t* block_tables, const int32_t* context_lens,
+                           int64_t num_seqs, int max_pages_per_seq, int pages_per_partition,
+                           int32_t* group_start, int32_t* group_seqs, int32_t* group_partitions,
+                           int32_t* seq_first_partition, int64_t* num_groups,
+                           int64_t* max_group_size, int64_t* max_group_partitions);
+
 /* Chained hash of one full page: the value registered for a page whose
  * parent has hash `parent` (0 for the first page) and whose tokens are
  * tokens[0..page_size).  Exposed so a router can compute prefix keys. */

@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     pa_chunk_attention,
     pa_decode,
     pa_decode_append,
+    pa_decode_cascade,
     pa_decode_reduce,
     pa_decode_valu,
     pa_export_pages,
@@ -19,4 +20,4 @@ from ._lib import (  # noqa: F401
     status_string,
     version,
 )
-from .pager import Pager, PagerError, page_hash  # noqa: F401,E402
+from .pager import Pager, PagerError, page_hash, prefix_groups  # noqa: F401,E402

@@ -40,6 +40,10 @@ _SIGNATURES = {
                          _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32,
                          _i64, _f32, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _i32,
                          _c_void_p],
+    "pa_decode_cascade": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                          _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32,
+                          _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
+                          _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p],
     "pa_chunk_attention": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                            _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
                            _f32, _i32, _c_void_p],
@@ -202,6 +206,39 @@ def pa_decode_append(out, query, key, value, slot_mapping, k_cache, v_cache, blo
         block_tables.shape[1], k_cache.shape[0], float(scale), int(partition_size), max_parts,
         _ptr(partial_out), _ptr(partial_max), _ptr(partial_sum), _dtype_code(query),
         _stream(stream)))
+
+
+def pa_decode_cascade(query, k_cache, v_cache, block_tables, context_lens, scale,
+                      partition_size, partial_out, partial_max, partial_sum, groups,
+                      key=None, value=None, slot_mapping=None, stream=None) -> None:
+    """Split-KV partials with shared prefixes read once per group; `groups`
+    holds device int32 tensors group_start / group_seqs / group_partitions /
+    seq_first_partition and the host ints num_groups / max_group_size /
+    max_group_partitions (paged_kv_decode_pa_amd.prefix_groups gives them on
+    the host).  Merge with pa_decode_reduce.  See include/pa.h."""
+    B, Hq, D = query.shape
+    Hkv = k_cache.shape[1]
+    if k_cache.shape[2:] != (PAGE_SIZE, D) or v_cache.shape[1:] != (Hkv, D, PAGE_SIZE):
+        raise ValueError("pool shape does not match query")
+    if block_tables.shape[0] != B or tuple(context_lens.shape) != (B,):
+        raise ValueError("block_tables / context_lens do not match the batch")
+    P = partial_max.shape[2]
+    if (partial_out.shape != (B, Hq, P, D) or partial_max.shape != (B, Hq, P)
+            or partial_sum.shape != (B, Hq, P)):
+        raise ValueError("partial buffers have the wrong shape")
+    if key is not None and (key.shape != (B, Hkv, D) or value.shape != key.shape
+                            or tuple(slot_mapping.shape) != (B,)):
+        raise ValueError("key, value and slot_mapping must hold one token per sequence")
+    lib = load()
+    _check("pa_decode_cascade", lib.pa_decode_cascade(
+        _ptr(query), _ptr(key), _ptr(value), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, D, PAGE_SIZE, block_tables.shape[1],
+        k_cache.shape[0], float(scale), int(partition_size), P, _ptr(partial_out),
+        _ptr(partial_max), _ptr(partial_sum), int(groups["num_groups"]),
+        int(groups["max_group_size"]), int(groups["max_group_partitions"]),
+        _ptr(groups.get("group_start")), _ptr(groups.get("group_seqs")),
+        _ptr(groups.get("group_partitions")), _ptr(groups.get("seq_first_partition")),
+        _dtype_code(query), _stream(stream)))
 
 
 def pa_chunk_attention(out, query, k_cache, v_cache, block_tables, context_lens, query_start,

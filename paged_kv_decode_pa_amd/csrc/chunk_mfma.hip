@@ -18,6 +18,8 @@
 // online-softmax states of each block merge through LDS in a fixed order.
 // Pages are read with cached loads: a long chunk's block groups reread the
 // same pages, and the kv-head-fastest unit order puts them on one XCD's L2.
+#include <limits.h>
+
 #include "page_stream.hpp"
 
 namespace pa {
@@ -190,6 +192,32 @@ __device__ inline void run_blocks(ColumnAttn<D> (&wa)[NB], PageStream<D>& ps, in
   }
 }
 
+// Every page of the stream is seen whole by every column (a shared prefix):
+// the mask-free step throughout, and no page is partial.
+template <int D, int NB>
+__device__ inline void run_clear(ColumnAttn<D> (&wa)[NB], PageStream<D>& ps, int page0, int lane) {
+  const int n = ps.count;
+  if (n <= 0) return;
+  auto base = [&](int k) { return (page0 + ps.step * k) * kPage; };
+  PageTile<D> ta, tb;
+  bool ok_a = ps.template issue<false>(ta, 0, lane);
+  bool ok_b = ps.template issue<false>(tb, 1, lane);
+  int k = 0;
+  for (; k + 3 < n; k += 2) {
+    if (ok_a) page_blocks<D, NB, false>(wa, ta, base(k));
+    ok_a = ps.template issue<false>(ta, k + 2, lane);
+    if (ok_b) page_blocks<D, NB, false>(wa, tb, base(k + 1));
+    ok_b = ps.template issue<false>(tb, k + 3, lane);
+  }
+  const int rem = n - k;
+  if (ok_a) page_blocks<D, NB, false>(wa, ta, base(k));
+  if (rem >= 2) {
+    const bool ok_c = rem == 3 && ps.template issue<false>(ta, k + 2, lane);
+    if (ok_b) page_blocks<D, NB, false>(wa, tb, base(k + 1));
+    if (ok_c) page_blocks<D, NB, false>(wa, ta, base(k + 2));
+  }
+}
+
 // LDS of the four-wave merge: per wave a reference and a sum per column and
 // the un-normalised accumulator [wave][column][D].
 __host__ __device__ inline size_t chunk_lds_bytes(int head_dim) {
@@ -296,6 +324,116 @@ __global__ __launch_bounds__(kBlock) void chunk_attention_kernel(ChunkParams p) 
   }
 }
 
+// Shared-prefix partials.  Unit = (group, shared partition, column group,
+// kv head), four waves; wave w takes the partition's pages w, w+4, ... from
+// the first member's block-table row (the members hold the same page ids
+// there).  Column c of the unit's blocks is member c / group, query head
+// c % group of the kv head.
+template <int D, int NB>
+__global__ __launch_bounds__(kBlock) void prefix_partial_kernel(PrefixParams p) {
+  extern __shared__ float smem[];
+  const int u = blockIdx.x;
+  if (u >= p.num_units) return;
+  const int kvh = u % p.num_kv_heads;
+  int rest = u / p.num_kv_heads;
+  const int cg = rest % p.column_groups;
+  rest /= p.column_groups;
+  const int part = rest % p.max_group_partitions;
+  const int g = rest / p.max_group_partitions;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, j = lane >> 4;
+  const int G = p.group;
+
+  const int gs = p.group_start[g];
+  const int members = p.group_start[g + 1] - gs;
+  const int cols = members * G;
+  const int c0 = cg * NB * 16;
+  if (members <= 0 || part >= p.group_partitions[g] || c0 >= cols) return;  // uniform
+  const int PP = p.pages_per_partition;
+  const int lo = part * PP;
+  const int hi = min(lo + PP, p.max_pages_per_seq);
+  const int first_seq = p.group_seqs[gs];
+  if (first_seq < 0 || first_seq >= p.num_seqs) return;  // uniform
+
+  PageStream<D> ps;
+  ps.table = p.block_tables + size_t(first_seq) * p.max_pages_per_seq;
+  ps.first = lo + w;
+  ps.step = kWaves;
+  ps.row_end = hi;
+  ps.kpool = static_cast<const char*>(p.k_cache);
+  ps.vpool = static_cast<const char*>(p.v_cache);
+  ps.num_pages = p.num_pages;
+  ps.num_kv_heads = p.num_kv_heads;
+  ps.kvh = kvh;
+  ps.koff = uint32_t(r * D + 8 * j) * 2u;
+  ps.voff = uint32_t(r * kPage + 4 * j) * 2u;
+  ps.start(lane);
+  ps.count = lo + w < hi ? (hi - lo - w + kWaves - 1) / kWaves : 0;
+
+  ColumnAttn<D> wa[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int c = c0 + 16 * nb + r;
+    int seq = c < cols ? p.group_seqs[gs + c / G] : -1;
+    const bool real = seq >= 0 && seq < p.num_seqs;
+    if (!real) seq = 0;
+    const int h = real ? c % G : 0;
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.query) +
+                           (size_t(seq) * p.num_q_heads + kvh * G + h) * D;
+    wa[nb].init(qrow, real, r, j, INT_MAX, p.scale_log2);
+  }
+  run_clear<D, NB>(wa, ps, lo + w, lane);
+
+  // Merge the four waves per column and write each member's partial for this
+  // partition, one block at a time through the same LDS.
+  float* lm = smem;
+  float* ll = smem + kWaves * 16;
+  float* la = smem + 2 * kWaves * 16;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int c_lo = c0 + 16 * nb;
+    if (c_lo >= cols) break;  // uniform
+    if (nb > 0) __syncthreads();
+    if (j == 0) {
+      lm[w * 16 + r] = wa[nb].m_run;
+      ll[w * 16 + r] = wa[nb].acc[D / 16][0];
+    }
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        la[(w * 16 + r) * D + 16 * db + 4 * j + e] = wa[nb].acc[db][e];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 16 * D; idx += kBlock) {
+      const int col = idx / D;
+      const int d = idx % D;
+      const int cc = c_lo + col;
+      if (cc >= cols) continue;
+      float M = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) M = fmaxf(M, lm[v * 16 + col]);
+      float wsum = 0.f, num = 0.f;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) {
+        const float mv = lm[v * 16 + col];
+        const float f = mv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv - M);
+        wsum += ll[v * 16 + col] * f;
+        num += la[(v * 16 + col) * D + d] * f;
+      }
+      const int seq = p.group_seqs[gs + cc / G];
+      if (seq < 0 || seq >= p.num_seqs) continue;
+      const size_t row =
+          (size_t(seq) * p.num_q_heads + kvh * G + cc % G) * p.num_partitions + part;
+      p.partial_out[row * D + d] = wsum > 0.f ? num / wsum : 0.f;
+      if (d == 0) {
+        p.partial_max[row] = M * kLn2;
+        p.partial_sum[row] = wsum;
+      }
+    }
+  }
+}
+
 template <int D>
 void launch_d(const ChunkParams& p, size_t lds, hipStream_t stream) {
   const dim3 grid(p.num_units);
@@ -308,6 +446,19 @@ void launch_d(const ChunkParams& p, size_t lds, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_prefix_partials(const PrefixParams& p, int head_dim, hipStream_t stream) {
+  const size_t lds = chunk_lds_bytes(head_dim);
+  const dim3 grid(p.num_units);
+#define PA_PREFIX(DD, NBB) prefix_partial_kernel<DD, NBB><<<grid, kBlock, lds, stream>>>(p)
+  if (head_dim == 128) {
+    if (p.blocks_per_wave == 1) PA_PREFIX(128, 1); else PA_PREFIX(128, 2);
+  } else {
+    if (p.blocks_per_wave == 1) PA_PREFIX(64, 1); else PA_PREFIX(64, 2);
+  }
+#undef PA_PREFIX
+  return hipGetLastError();
+}
 
 hipError_t launch_chunk_attention(const ChunkParams& p, int head_dim, hipStream_t stream) {
   const size_t lds = chunk_lds_bytes(head_dim);

@@ -310,20 +310,27 @@ template <int NC>
 __device__ bool split_unit(const DecodeParams& p, int useq, int lane, int& seq, int& part,
                            int& seq_pages) {
   const int PP = p.pages_per_partition;
-  int pages[NC], nfull[NC], hasp[NC];
+  int pages[NC], nfull[NC], hasp[NC], first[NC];
   load_pages<NC>(p, lane, pages);
+#pragma unroll
+  for (int c = 0; c < NC; ++c)  // partitions computed elsewhere (a shared prefix)
+    first[c] = p.first_partition ? max(p.first_partition[min(64 * c + lane, p.num_seqs - 1)], 0)
+                                 : 0;
   int full_total = 0, part_total = 0;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int nparts = min((pages[c] + PP - 1) / PP, p.num_partitions);
-    nfull[c] = min(pages[c] / PP, p.num_partitions);
-    hasp[c] = nparts > nfull[c] ? 1 : 0;
+    const int full = min(pages[c] / PP, p.num_partitions);
+    first[c] = min(first[c], full);  // only whole partitions are skipped
+    nfull[c] = full - first[c];      // counted from the first partition computed here
+    hasp[c] = nparts > full ? 1 : 0;
     full_total += nfull[c];
     part_total += hasp[c];
   }
   full_total = wave_sum(full_total);
   part_total = wave_sum(part_total);
   seq = -1;
+  part = 0;
   if (useq < full_total) {
     // Smallest p with sum_b min(nfull_b, p + 1) > useq.
     int lo = 0, hi = p.num_partitions;  // O(lo) <= useq < O(hi)
@@ -338,12 +345,14 @@ __device__ bool split_unit(const DecodeParams& p, int useq, int lane, int& seq, 
 #pragma unroll
     for (int c = 0; c < NC; ++c) o += min(nfull[c], lo);
     int k = useq - wave_sum(o);  // rank among the sequences with a full partition lo
-    part = lo;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const uint64_t m = __ballot(nfull[c] > lo);
       const int n = __popcll(m);
-      if (seq < 0 && k < n && k >= 0) seq = 64 * c + kth_set_lane(m, k, lane);
+      if (seq < 0 && k < n && k >= 0) {
+        seq = 64 * c + kth_set_lane(m, k, lane);
+        part = lo + __builtin_amdgcn_readlane(first[c], seq - 64 * c);
+      }
       k -= n;
     }
   } else {
@@ -354,7 +363,7 @@ __device__ bool split_unit(const DecodeParams& p, int useq, int lane, int& seq, 
       const int n = __popcll(m);
       if (seq < 0 && k < n && k >= 0) {
         seq = 64 * c + kth_set_lane(m, k, lane);
-        part = __builtin_amdgcn_readlane(nfull[c], seq - 64 * c);
+        part = __builtin_amdgcn_readlane(nfull[c] + first[c], seq - 64 * c);
       }
       k -= n;
     }
@@ -412,6 +421,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   } else {
     seq = useq % p.num_seqs;  // plain grid: partitions past a context exit below
     part = useq / p.num_seqs;
+    if (p.first_partition && part < p.first_partition[seq]) return;  // computed elsewhere
   }
   seq = __builtin_amdgcn_readfirstlane(seq);
   part = __builtin_amdgcn_readfirstlane(part);
@@ -467,22 +477,32 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
 
 // ---------------------------------------------------------------- single pass
 // Unit = (sequence, kv head), four waves; wave w takes pages w, w+4, ...
+// With partitions (the four-wave split-KV units, chosen when the batch has
+// few units for the machine, as a shared-prefix step's suffixes do), unit =
+// (sequence, partition, kv head) over the partition's pages, and the merged
+// state is written as that partition's partial.
 template <int D>
 __global__ __launch_bounds__(kBlock) void decode_whole_kernel(DecodeParams p) {
   extern __shared__ float smem[];
   int seq, kvh, part;
   if (!unit_of_block(p, seq, kvh, part)) return;
+  if (p.first_partition && part < p.first_partition[seq]) return;  // computed elsewhere
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, j = lane >> 4;
   const int G = p.group;
+  const int PP = p.pages_per_partition;
+  const int lo0 = part * PP;  // 0 for the single pass
 
   // Every wave requests the new token with its first loads (the length, which
   // says which wave reads the last page, is not known yet).
   const bool appends = p.new_key != nullptr;
   NewToken<D> nt;
   if (appends) nt.request(p, seq, kvh, lane);
-  PageStream<D> ps = make_stream<D>(p, seq, kvh, w, kWaves, p.max_pages_per_seq, lane);
+  PageStream<D> ps = make_stream<D>(p, seq, kvh, lo0 + w, kWaves,
+                                    PP > 0 ? min(lo0 + PP, p.max_pages_per_seq)
+                                           : p.max_pages_per_seq,
+                                    lane);
   const int L = p.context_lens[seq];
   WaveAttn<D> wa;
   wa.init(static_cast<const uint16_t*>(p.query) + (size_t(seq) * p.num_q_heads + kvh * G + r) * D,
@@ -490,15 +510,16 @@ __global__ __launch_bounds__(kBlock) void decode_whole_kernel(DecodeParams p) {
 
   int lo, hi;
   if (!unit_pages(p, seq, part, L, lo, hi)) {
-    store_zeros<uint16_t, D>(p, seq, kvh);
-    return;
+    if (PP == 0) store_zeros<uint16_t, D>(p, seq, kvh);
+    return;  // a partition past the context writes nothing
   }
-  const bool writes = appends && (hi - 1) % kWaves == w && nt.valid(p);
-  ps.count = w < hi ? (hi - w + kWaves - 1) / kWaves : 0;
+  const int n = min((L + kPage - 1) / kPage, p.max_pages_per_seq);
+  const bool writes = appends && hi == n && (hi - 1 - lo) % kWaves == w && nt.valid(p);
+  ps.count = w < hi - lo ? (hi - lo - w + kWaves - 1) / kWaves : 0;
   // Cached loads throughout: with four waves per unit this kernel runs far
   // fewer waves than the split one, and the nontemporal hint measured up to
   // 25% slower here (long contexts of the 256-sequence batch).
-  wa.run(ps, w, L, lane, /*shared=*/true, writes, nt);
+  wa.run(ps, lo + w, L, lane, /*shared=*/true, writes, nt);
   if (writes) nt.store(p, kvh, lane);
 
   MergeLds lds(smem);
@@ -517,7 +538,7 @@ __global__ __launch_bounds__(kBlock) void decode_whole_kernel(DecodeParams p) {
 
 template <int D>
 hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
-  if (p.pages_per_partition > 0) {
+  if (p.pages_per_partition > 0 && !p.four_wave_units) {
     switch (plan_chunks_for(p.num_seqs)) {
       case 1: decode_split_kernel<D, 1><<<dim3(p.num_units), 64, 0, stream>>>(p); break;
       case 4: decode_split_kernel<D, 4><<<dim3(p.num_units), 64, 0, stream>>>(p); break;

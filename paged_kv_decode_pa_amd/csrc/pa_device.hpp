@@ -39,6 +39,44 @@ struct DecodeParams {
   const void* new_key;      // [num_seqs][num_kv_heads][head_dim]
   const void* new_value;    // [num_seqs][num_kv_heads][head_dim]
   const int64_t* new_slots; // [num_seqs]; < 0 writes nothing
+  // Partitions below first_partition[b] of sequence b are computed elsewhere
+  // (a shared prefix, once per group); NULL: every partition here.
+  const int32_t* first_partition;
+  // Split-KV with four waves per (sequence, partition, kv head) unit instead
+  // of one: for batches with few units for the machine.
+  bool four_wave_units;
+};
+
+// Split-KV partials of the pages a group of sequences shares from position 0:
+// each shared partition is read once per (group, kv head), its tiles serving
+// every member's query heads as the columns of the matrix tiles, and every
+// member's partial for that partition is written as the decode's split
+// kernel would (o normalised, m in natural-log units, l).
+struct PrefixParams {
+  const void* query;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  float* partial_out;
+  float* partial_max;
+  float* partial_sum;
+  const int32_t* group_start;       // [num_groups + 1]: members are group_seqs[start[g] ..]
+  const int32_t* group_seqs;        // batch indices
+  const int32_t* group_partitions;  // [num_groups]: shared partitions from position 0
+  int num_groups;
+  int num_seqs;                     // members outside [0, num_seqs) are skipped
+  int num_q_heads;
+  int num_kv_heads;
+  int group;                        // query heads per kv head
+  int max_pages_per_seq;
+  int64_t num_pages;
+  float scale_log2;
+  int pages_per_partition;
+  int num_partitions;               // partition slots per row of the partial arrays
+  int max_group_partitions;         // grid bound
+  int blocks_per_wave;              // 16-column blocks a wave carries (1 or 2)
+  int column_groups;                // ceil(max members * group / (16 * blocks_per_wave))
+  int num_units;
 };
 
 // Multi-token causal attention over the same cache: sequence b's new query

@@ -322,6 +322,67 @@ int pa_pager_drain_events(pa_pager* pg, int32_t* kinds, int64_t* pages, uint64_t
   return PA_PAGER_OK;
 }
 
+int pa_pager_prefix_groups(const int32_t* block_tables, const int32_t* context_lens,
+                           int64_t num_seqs, int max_pages_per_seq, int pages_per_partition,
+                           int32_t* group_start, int32_t* group_seqs, int32_t* group_partitions,
+                           int32_t* seq_first_partition, int64_t* num_groups,
+                           int64_t* max_group_size, int64_t* max_group_partitions) {
+  if (num_seqs < 0 || max_pages_per_seq <= 0 || pages_per_partition <= 0 || !num_groups ||
+      !max_group_size || !max_group_partitions || !group_start)
+    return PA_PAGER_INVALID_ARGUMENT;
+  if (num_seqs > 0 && (!block_tables || !context_lens || !group_seqs || !group_partitions ||
+                       !seq_first_partition))
+    return PA_PAGER_INVALID_ARGUMENT;
+  const int P = 16;
+  auto row = [&](int64_t b) { return block_tables + b * max_pages_per_seq; };
+  auto whole = [&](int64_t b) {  // pages wholly before the last token
+    const int L = context_lens[b];
+    return std::min(L > 0 ? (L - 1) / P : 0, max_pages_per_seq);
+  };
+  // Buckets by the page in column 0, in order of first appearance.
+  std::unordered_map<int32_t, size_t> bucket_of;
+  std::vector<std::vector<int64_t>> buckets;
+  for (int64_t b = 0; b < num_seqs; ++b) {
+    seq_first_partition[b] = 0;
+    if (whole(b) < pages_per_partition) continue;
+    auto it = bucket_of.find(row(b)[0]);
+    if (it == bucket_of.end()) {
+      bucket_of.emplace(row(b)[0], buckets.size());
+      buckets.push_back({b});
+    } else {
+      buckets[it->second].push_back(b);
+    }
+  }
+  int64_t g = 0, at = 0, max_size = 0, max_parts = 0;
+  group_start[0] = 0;
+  for (const auto& members : buckets) {
+    if (members.size() < 2) continue;
+    const int32_t* first = row(members[0]);
+    int lcp = whole(members[0]);
+    for (size_t i = 1; i < members.size(); ++i) {
+      const int32_t* r = row(members[i]);
+      const int lim = std::min(lcp, whole(members[i]));
+      int l = 0;
+      while (l < lim && r[l] == first[l]) ++l;
+      lcp = l;
+    }
+    const int parts = lcp / pages_per_partition;
+    if (parts < 1) continue;
+    for (int64_t b : members) {
+      group_seqs[at++] = int32_t(b);
+      seq_first_partition[b] = parts;
+    }
+    group_partitions[g] = parts;
+    group_start[++g] = int32_t(at);
+    max_size = std::max<int64_t>(max_size, int64_t(members.size()));
+    max_parts = std::max<int64_t>(max_parts, parts);
+  }
+  *num_groups = g;
+  *max_group_size = max_size;
+  *max_group_partitions = max_parts;
+  return PA_PAGER_OK;
+}
+
 uint64_t pa_pager_page_hash(uint64_t parent, const int32_t* tokens, int page_size) {
   if (!tokens || page_size <= 0) return 0;
   return chain_hash(parent, tokens, page_size);

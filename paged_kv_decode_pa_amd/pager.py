@@ -60,6 +60,9 @@ def load(path: str = PAGER_LIB_PATH) -> ctypes.CDLL:
         "pa_pager_get_stats": ([_P, ctypes.POINTER(_Stats)], ctypes.c_int),
         "pa_pager_drain_events": ([_P, _I32P, _I64P, _U64P, ctypes.c_int64, _I64P], ctypes.c_int),
         "pa_pager_page_hash": ([ctypes.c_uint64, _I32P, ctypes.c_int], ctypes.c_uint64),
+        "pa_pager_prefix_groups": ([_I32P, _I32P, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                    _I32P, _I32P, _I32P, _I32P, _I64P, _I64P, _I64P],
+                                   ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -76,6 +79,28 @@ def _ptr(a: np.ndarray, ctype=None):
 def page_hash(parent: int, tokens: Sequence[int]) -> int:
     t = np.ascontiguousarray(tokens, dtype=np.int32)
     return int(load().pa_pager_page_hash(parent, _ptr(t, ctypes.c_int32), len(t)))
+
+
+def prefix_groups(block_tables, context_lens, pages_per_partition: int) -> dict:
+    """Groups of sequences sharing their first pages (host arrays), in the
+    form pa_decode_cascade takes; see pa_pager_prefix_groups."""
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    B, max_pages = bt.shape
+    start = np.zeros(B + 1, dtype=np.int32)
+    seqs = np.zeros(max(B, 1), dtype=np.int32)
+    parts = np.zeros(max(B, 1), dtype=np.int32)
+    first = np.zeros(max(B, 1), dtype=np.int32)
+    ng, mg, mp = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    st = load().pa_pager_prefix_groups(
+        _ptr(bt), _ptr(lens), B, max_pages, int(pages_per_partition), _ptr(start), _ptr(seqs),
+        _ptr(parts), _ptr(first), ctypes.byref(ng), ctypes.byref(mg), ctypes.byref(mp))
+    if st != OK:
+        raise PagerError("pa_pager_prefix_groups", st)
+    n = ng.value
+    return {"num_groups": n, "max_group_size": mg.value, "max_group_partitions": mp.value,
+            "group_start": start[:n + 1].copy(), "group_seqs": seqs[:start[n]].copy(),
+            "group_partitions": parts[:n].copy(), "seq_first_partition": first[:B].copy()}
 
 
 class Pager:

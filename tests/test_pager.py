@@ -274,3 +274,63 @@ def test_append_batch_equals_appends_in_order():
         assert a.stats() == m.stats()
         if status:
             break
+
+
+def _prefix_groups_by_hand(tables, lens, pp):
+    """Plain rendering of the grouping rule: same page in column 0, then the
+    longest common run of page ids over every member's pages that lie wholly
+    before its last token, in whole partitions; groups of 2+ members."""
+    B = len(lens)
+    whole = [min(max(int(L) - 1, 0) // 16, tables.shape[1]) for L in lens]
+    order, buckets = [], {}
+    for b in range(B):
+        if whole[b] < pp:
+            continue
+        key = int(tables[b, 0])
+        if key not in buckets:
+            buckets[key] = []
+            order.append(key)
+        buckets[key].append(b)
+    groups, first = [], [0] * B
+    for key in order:
+        m = buckets[key]
+        if len(m) < 2:
+            continue
+        lcp = whole[m[0]]
+        for b in m[1:]:
+            l = 0
+            while l < min(lcp, whole[b]) and tables[b, l] == tables[m[0], l]:
+                l += 1
+            lcp = l
+        if lcp // pp >= 1:
+            groups.append((m, lcp // pp))
+            for b in m:
+                first[b] = lcp // pp
+    return groups, first
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_prefix_groups_match_the_rule(seed):
+    rng = np.random.default_rng(seed)
+    B, max_pages, pp = int(rng.integers(1, 40)), 40, int(rng.choice([1, 2, 4]))
+    stems = [rng.permutation(1000)[:max_pages] for _ in range(4)]
+    tables = np.full((B, max_pages), -1, dtype=np.int32)
+    lens = rng.integers(0, max_pages * 16, size=B).astype(np.int32)
+    fresh = 2000
+    for b in range(B):
+        n = -(-int(lens[b]) // 16)
+        s = stems[int(rng.integers(4))]
+        cut = int(rng.integers(0, n + 1))
+        tables[b, :cut] = s[:cut]
+        tables[b, cut:n] = np.arange(fresh, fresh + n - cut)
+        fresh += n - cut
+    got = pa.prefix_groups(tables, lens, pp)
+    groups, first = _prefix_groups_by_hand(tables, lens, pp)
+    assert got["num_groups"] == len(groups)
+    starts = got["group_start"].tolist()
+    for g, (members, parts) in enumerate(groups):
+        assert got["group_seqs"][starts[g]:starts[g + 1]].tolist() == members
+        assert int(got["group_partitions"][g]) == parts
+    assert got["seq_first_partition"].tolist() == first
+    assert got["max_group_size"] == max([len(m) for m, _ in groups], default=0)
+    assert got["max_group_partitions"] == max([p for _, p in groups], default=0)
