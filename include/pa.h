@@ -229,16 +229,25 @@ int pa_decode_append(void* out, const void* query, const void* key, const void* 
  * those pages lies inside every member's context.  For each such partition and
  * kv head one work unit reads the pages once and computes every member's
  * partial for it: the members' query heads are the columns of the matrix
- * tiles, up to 64 per wave.  Then the ordinary split-KV kernel computes each
- * sequence's partitions from seq_first_partition[b] on (0 for sequences in no
- * group).  With key/value/slot_mapping non-NULL it also writes the step's new
- * token first, as pa_decode_append does.  The partial arrays end up as
- * pa_decode (split) writes them: merge them with pa_decode_reduce.
+ * tiles, up to 32 per wave.  Then a second launch computes each sequence's
+ * partitions from seq_first_partition[b] on (0 for sequences in no group),
+ * four waves per (sequence, partition, kv head).  With key/value/slot_mapping
+ * non-NULL that launch also writes the step's new token, as pa_decode_append
+ * does.  The partial arrays end up as pa_decode (split) writes them: merge
+ * them with pa_decode_reduce.
  *
  *   num_groups, max_group_size, max_group_partitions  host bounds that size
  *               the grid: groups of more members or partitions are not fully
  *               computed (unspecified results).  max_group_partitions must
  *               not exceed max_num_partitions.
+ *   max_suffix_partitions  host bound on min(ceil(L_b / partition_size),
+ *               max_num_partitions) - seq_first_partition[b] over the batch:
+ *               the second launch's grid holds that many partitions per
+ *               sequence, counted from its first.  A smaller value than the
+ *               true maximum leaves partitions uncomputed (unspecified
+ *               results); 0 means max_num_partitions (always enough, at the
+ *               cost of workgroups that find nothing to do).
+ *               pa_pager_prefix_groups returns it.
  *   group_start [num_groups + 1], group_seqs, group_partitions [num_groups],
  *   seq_first_partition [num_seqs]: int32, device.  seq_first_partition[b]
  *               must equal group_partitions of b's group (0 outside groups).
@@ -248,8 +257,8 @@ int pa_decode_append(void* out, const void* query, const void* key, const void* 
  * deterministic.  Members outside [0, num_seqs) are skipped.  bf16 only:
  * other dtypes return PA_ERR_UNSUPPORTED.  num_groups == 0 is pa_decode (or
  * pa_decode_append).  Host-checkable errors as for pa_decode, plus
- * PA_ERR_INVALID_ARGUMENT for partition_size 0, NULL group arrays with
- * num_groups > 0, or key/value/slot_mapping given only in part.
+ * PA_ERR_INVALID_ARGUMENT for partition_size 0, a negative bound, NULL group
+ * arrays with num_groups > 0, or key/value/slot_mapping given only in part.
  */
 int pa_decode_cascade(const void* query, const void* key, const void* value,
                       const int64_t* slot_mapping, void* k_cache, void* v_cache,
@@ -258,9 +267,10 @@ int pa_decode_cascade(const void* query, const void* key, const void* value,
                       int max_pages_per_seq, int64_t num_pages, float scale, int partition_size,
                       int max_num_partitions, float* partial_out, float* partial_max,
                       float* partial_sum, int num_groups, int max_group_size,
-                      int max_group_partitions, const int32_t* group_start,
-                      const int32_t* group_seqs, const int32_t* group_partitions,
-                      const int32_t* seq_first_partition, int dtype, void* stream);
+                      int max_group_partitions, int max_suffix_partitions,
+                      const int32_t* group_start, const int32_t* group_seqs,
+                      const int32_t* group_partitions, const int32_t* seq_first_partition,
+                      int dtype, void* stream);
 
 /*
  * pa_decode_valu — pa_decode with the vector-ALU kernel forced.

@@ -139,13 +139,17 @@ int pa_pager_drain_events(pa_pager* pager, int32_t* kinds, int64_t* pages, uint6
  * are dropped.  Groups are ordered by their first member and members by batch
  * index.  Outputs (host; sized for the worst case): group_start [num_seqs +
  * 1], group_seqs [num_seqs], group_partitions [num_seqs], seq_first_partition
- * [num_seqs] (0 outside groups); *num_groups, *max_group_size and
- * *max_group_partitions. */
+ * [num_seqs] (0 outside groups); *num_groups, *max_group_size,
+ * *max_group_partitions, and *max_suffix_partitions: the most partitions any
+ * sequence has from its seq_first_partition on (ceil(min(ceil(L / 16),
+ * max_pages_per_seq) / pages_per_partition) - first), the bound
+ * pa_decode_cascade sizes its second launch by. */
 int pa_pager_prefix_groups(const int32_t* block_tables, const int32_t* context_lens,
                            int64_t num_seqs, int max_pages_per_seq, int pages_per_partition,
                            int32_t* group_start, int32_t* group_seqs, int32_t* group_partitions,
                            int32_t* seq_first_partition, int64_t* num_groups,
-                           int64_t* max_group_size, int64_t* max_group_partitions);
+                           int64_t* max_group_size, int64_t* max_group_partitions,
+                           int64_t* max_suffix_partitions);
 
 /* Chained hash of one full page: the value registered for a page whose
  * parent has hash `parent` (0 for the first page) and whose tokens are

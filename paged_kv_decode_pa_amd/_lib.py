@@ -42,7 +42,7 @@ _SIGNATURES = {
                          _c_void_p],
     "pa_decode_cascade": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                           _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _f32,
-                          _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
+                          _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32,
                           _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p],
     "pa_chunk_attention": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                            _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
@@ -214,8 +214,8 @@ def pa_decode_cascade(query, k_cache, v_cache, block_tables, context_lens, scale
     """Split-KV partials with shared prefixes read once per group; `groups`
     holds device int32 tensors group_start / group_seqs / group_partitions /
     seq_first_partition and the host ints num_groups / max_group_size /
-    max_group_partitions (paged_kv_decode_pa_amd.prefix_groups gives them on
-    the host).  Merge with pa_decode_reduce.  See include/pa.h."""
+    max_group_partitions / max_suffix_partitions (optional: 0 = no bound)
+    (paged_kv_decode_pa_amd.prefix_groups gives them on the host).  Merge with pa_decode_reduce.  See include/pa.h."""
     B, Hq, D = query.shape
     Hkv = k_cache.shape[1]
     if k_cache.shape[2:] != (PAGE_SIZE, D) or v_cache.shape[1:] != (Hkv, D, PAGE_SIZE):
@@ -236,6 +236,7 @@ def pa_decode_cascade(query, k_cache, v_cache, block_tables, context_lens, scale
         k_cache.shape[0], float(scale), int(partition_size), P, _ptr(partial_out),
         _ptr(partial_max), _ptr(partial_sum), int(groups["num_groups"]),
         int(groups["max_group_size"]), int(groups["max_group_partitions"]),
+        int(groups.get("max_suffix_partitions", 0)),
         _ptr(groups.get("group_start")), _ptr(groups.get("group_seqs")),
         _ptr(groups.get("group_partitions")), _ptr(groups.get("seq_first_partition")),
         _dtype_code(query), _stream(stream)))

@@ -221,7 +221,7 @@ __device__ inline void run_clear(ColumnAttn<D> (&wa)[NB], PageStream<D>& ps, int
 // LDS of the four-wave merge: per wave a reference and a sum per column and
 // the un-normalised accumulator [wave][column][D].
 __host__ __device__ inline size_t chunk_lds_bytes(int head_dim) {
-  return sizeof(float) * (2 * kWaves * 16 + size_t(kWaves) * 16 * head_dim);
+  return sizeof(float) * (2 * kWaves * 16 + size_t(kWaves) * 16 * (head_dim + kAccPad));
 }
 
 template <int D, int NB>
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(kBlock) void chunk_attention_kernel(ChunkParams p) 
   // one block at a time through the same LDS.
   float* lm = smem;                       // [kWaves][16]
   float* ll = smem + kWaves * 16;         // [kWaves][16]
-  float* la = smem + 2 * kWaves * 16;     // [kWaves][16][D]
+  float* la = smem + 2 * kWaves * 16;     // [kWaves][16][D + kAccPad]
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int c_lo = c0 + 16 * nb;
@@ -296,9 +296,8 @@ __global__ __launch_bounds__(kBlock) void chunk_attention_kernel(ChunkParams p) 
     }
 #pragma unroll
     for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        la[(w * 16 + r) * D + 16 * db + 4 * j + e] = wa[nb].acc[db][e];
+      *reinterpret_cast<f32x4*>(la + (w * 16 + r) * (D + kAccPad) + 16 * db + 4 * j) =
+          wa[nb].acc[db];
     __syncthreads();
     for (int idx = threadIdx.x; idx < 16 * D; idx += kBlock) {
       const int col = idx / D;
@@ -314,7 +313,7 @@ __global__ __launch_bounds__(kBlock) void chunk_attention_kernel(ChunkParams p) 
         const float mv = lm[v * 16 + col];
         const float f = mv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv - M);
         wsum += ll[v * 16 + col] * f;
-        num += la[(v * 16 + col) * D + d] * f;
+        num += la[(v * 16 + col) * (D + kAccPad) + d] * f;
       }
       const int row = q0 + cc / G;
       const int head = kvh * G + cc % G;
@@ -325,12 +324,14 @@ __global__ __launch_bounds__(kBlock) void chunk_attention_kernel(ChunkParams p) 
 }
 
 // Shared-prefix partials.  Unit = (group, shared partition, column group,
-// kv head), four waves; wave w takes the partition's pages w, w+4, ... from
-// the first member's block-table row (the members hold the same page ids
-// there).  Column c of the unit's blocks is member c / group, query head
-// c % group of the kv head.
-template <int D, int NB>
-__global__ __launch_bounds__(kBlock) void prefix_partial_kernel(PrefixParams p) {
+// kv head), W waves; wave w takes the partition's pages w, w+W, ... from the
+// first member's block-table row (the members hold the same page ids there).
+// Column c of the unit's blocks is member c / group, query head c % group of
+// the kv head.  Eight waves halve each wave's chain of dependent page steps
+// against four: the pass has few units (groups x shared partitions), and its
+// time is those chains.
+template <int D, int NB, int W>
+__global__ __launch_bounds__(64 * W) void prefix_partial_kernel(PrefixParams p) {
   extern __shared__ float smem[];
   const int u = blockIdx.x;
   if (u >= p.num_units) return;
@@ -359,7 +360,7 @@ __global__ __launch_bounds__(kBlock) void prefix_partial_kernel(PrefixParams p) 
   PageStream<D> ps;
   ps.table = p.block_tables + size_t(first_seq) * p.max_pages_per_seq;
   ps.first = lo + w;
-  ps.step = kWaves;
+  ps.step = W;
   ps.row_end = hi;
   ps.kpool = static_cast<const char*>(p.k_cache);
   ps.vpool = static_cast<const char*>(p.v_cache);
@@ -369,14 +370,16 @@ __global__ __launch_bounds__(kBlock) void prefix_partial_kernel(PrefixParams p) 
   ps.koff = uint32_t(r * D + 8 * j) * 2u;
   ps.voff = uint32_t(r * kPage + 4 * j) * 2u;
   ps.start(lane);
-  ps.count = lo + w < hi ? (hi - lo - w + kWaves - 1) / kWaves : 0;
+  ps.count = lo + w < hi ? (hi - lo - w + W - 1) / W : 0;
 
   ColumnAttn<D> wa[NB];
+  int col_seq[NB];  // batch index of column r's member, -1 for no member
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int c = c0 + 16 * nb + r;
     int seq = c < cols ? p.group_seqs[gs + c / G] : -1;
     const bool real = seq >= 0 && seq < p.num_seqs;
+    col_seq[nb] = real ? seq : -1;
     if (!real) seq = 0;
     const int h = real ? c % G : 0;
     const uint16_t* qrow = static_cast<const uint16_t*>(p.query) +
@@ -385,11 +388,17 @@ __global__ __launch_bounds__(kBlock) void prefix_partial_kernel(PrefixParams p) 
   }
   run_clear<D, NB>(wa, ps, lo + w, lane);
 
-  // Merge the four waves per column and write each member's partial for this
-  // partition, one block at a time through the same LDS.
-  float* lm = smem;
-  float* ll = smem + kWaves * 16;
-  float* la = smem + 2 * kWaves * 16;
+  // Merge the W waves per column and write each member's partial for this
+  // partition, one block at a time through the same LDS.  The columns'
+  // members go to LDS once, so the stores wait on no global load.
+  float* lm = smem;                 // [W][16]
+  float* ll = smem + W * 16;        // [W][16]
+  float* la = smem + 2 * W * 16;    // [W][16][D + kAccPad]
+  int* lseq = reinterpret_cast<int*>(la + W * 16 * (D + kAccPad));  // [NB][16]
+  if (w == 0 && j == 0) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) lseq[nb * 16 + r] = col_seq[nb];
+  }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int c_lo = c0 + 16 * nb;
@@ -401,31 +410,36 @@ __global__ __launch_bounds__(kBlock) void prefix_partial_kernel(PrefixParams p) 
     }
 #pragma unroll
     for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        la[(w * 16 + r) * D + 16 * db + 4 * j + e] = wa[nb].acc[db][e];
+      *reinterpret_cast<f32x4*>(la + (w * 16 + r) * (D + kAccPad) + 16 * db + 4 * j) =
+          wa[nb].acc[db];
     __syncthreads();
-    for (int idx = threadIdx.x; idx < 16 * D; idx += kBlock) {
-      const int col = idx / D;
-      const int d = idx % D;
+    // Thread: one column's four consecutive dims per step.
+    for (int idx = threadIdx.x; idx < 16 * (D / 4); idx += 64 * W) {
+      const int col = idx / (D / 4);
+      const int d = 4 * (idx % (D / 4));
       const int cc = c_lo + col;
-      if (cc >= cols) continue;
+      const int seq = lseq[nb * 16 + col];
+      if (cc >= cols || seq < 0) continue;
       float M = -INFINITY;
 #pragma unroll
-      for (int v = 0; v < kWaves; ++v) M = fmaxf(M, lm[v * 16 + col]);
-      float wsum = 0.f, num = 0.f;
+      for (int v = 0; v < W; ++v) M = fmaxf(M, lm[v * 16 + col]);
+      float wsum = 0.f;
+      f32x4 num = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int v = 0; v < kWaves; ++v) {
+      for (int v = 0; v < W; ++v) {
         const float mv = lm[v * 16 + col];
         const float f = mv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv - M);
         wsum += ll[v * 16 + col] * f;
-        num += la[(v * 16 + col) * D + d] * f;
+        num += *reinterpret_cast<const f32x4*>(la + (v * 16 + col) * (D + kAccPad) + d) * f;
       }
-      const int seq = p.group_seqs[gs + cc / G];
-      if (seq < 0 || seq >= p.num_seqs) continue;
       const size_t row =
           (size_t(seq) * p.num_q_heads + kvh * G + cc % G) * p.num_partitions + part;
-      p.partial_out[row * D + d] = wsum > 0.f ? num / wsum : 0.f;
+      f32x4 o = {0.f, 0.f, 0.f, 0.f};
+      if (wsum > 0.f) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = num[e] / wsum;
+      }
+      *reinterpret_cast<f32x4*>(p.partial_out + row * D + d) = o;
       if (d == 0) {
         p.partial_max[row] = M * kLn2;
         p.partial_sum[row] = wsum;
@@ -448,14 +462,20 @@ void launch_d(const ChunkParams& p, size_t lds, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_prefix_partials(const PrefixParams& p, int head_dim, hipStream_t stream) {
-  const size_t lds = chunk_lds_bytes(head_dim);
   const dim3 grid(p.num_units);
-#define PA_PREFIX(DD, NBB) prefix_partial_kernel<DD, NBB><<<grid, kBlock, lds, stream>>>(p)
+  const int W = p.waves;
+  const size_t lds = sizeof(float) * (2 * W * 16 + size_t(W) * 16 * (head_dim + kAccPad)) +
+                     sizeof(int) * 2 * 16;  // + the columns' members, two blocks at most
+#define PA_PREFIX(DD, NBB, WW) \
+  prefix_partial_kernel<DD, NBB, WW><<<grid, 64 * WW, lds, stream>>>(p)
+#define PA_PREFIX_W(DD, NBB) \
+  do { if (W == 8) PA_PREFIX(DD, NBB, 8); else PA_PREFIX(DD, NBB, 4); } while (0)
   if (head_dim == 128) {
-    if (p.blocks_per_wave == 1) PA_PREFIX(128, 1); else PA_PREFIX(128, 2);
+    if (p.blocks_per_wave == 1) PA_PREFIX_W(128, 1); else PA_PREFIX_W(128, 2);
   } else {
-    if (p.blocks_per_wave == 1) PA_PREFIX(64, 1); else PA_PREFIX(64, 2);
+    if (p.blocks_per_wave == 1) PA_PREFIX_W(64, 1); else PA_PREFIX_W(64, 2);
   }
+#undef PA_PREFIX_W
 #undef PA_PREFIX
   return hipGetLastError();
 }

@@ -486,7 +486,8 @@ __global__ __launch_bounds__(kBlock) void decode_whole_kernel(DecodeParams p) {
   extern __shared__ float smem[];
   int seq, kvh, part;
   if (!unit_of_block(p, seq, kvh, part)) return;
-  if (p.first_partition && part < p.first_partition[seq]) return;  // computed elsewhere
+  if (p.first_partition)  // partitions below it are computed elsewhere
+    part += min(max(p.first_partition[seq], 0), p.num_partitions);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, j = lane >> 4;
@@ -530,8 +531,8 @@ __global__ __launch_bounds__(kBlock) void decode_whole_kernel(DecodeParams p) {
     }
 #pragma unroll
     for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) lds.acc[(w * G + r) * D + 16 * db + 4 * j + e] = wa.acc[db][e];
+      *reinterpret_cast<f32x4*>(lds.acc + (w * G + r) * (D + kAccPad) + 16 * db + 4 * j) =
+          wa.acc[db];
   }
   merge_and_store<uint16_t, D>(p, lds, seq, kvh, part);
 }

@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kBlock) void decode_valu_kernel(DecodeParams p) {
       lds.l[w * kMaxGroup + h] = l;
     }
 #pragma unroll
-    for (int vi = 0; vi < VD; ++vi) lds.acc[(w * G + h) * D + lane + 64 * vi] = acc[h][vi];
+    for (int vi = 0; vi < VD; ++vi) lds.acc[(w * G + h) * (D + kAccPad) + lane + 64 * vi] = acc[h][vi];
   }
   merge_and_store<T, D>(p, lds, seq, kvh, part);
 }

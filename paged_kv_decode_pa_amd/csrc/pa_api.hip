@@ -28,6 +28,7 @@ hipError_t launch_decode_reduce(void* out, const float* part_out, const float* p
 namespace {
 
 constexpr int kVersion = 10000;  // 1.0.0
+constexpr int kPrefixWaves = 4;  // waves per shared-prefix unit
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -50,7 +51,8 @@ int decode_impl(DecodeKernel which, void* out, const void* query, const void* k_
                 int max_num_partitions, float* partial_out, float* partial_max,
                 float* partial_sum, int dtype, void* stream, const void* new_key = nullptr,
                 const void* new_value = nullptr, const int64_t* new_slots = nullptr,
-                const int32_t* first_partition = nullptr, bool four_wave_units = false) {
+                const int32_t* first_partition = nullptr, bool four_wave_units = false,
+                int grid_partitions = 0) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_pages_per_seq <= 0 ||
       num_pages <= 0 || partition_size < 0)
     return PA_ERR_INVALID_ARGUMENT;
@@ -73,7 +75,14 @@ int decode_impl(DecodeKernel which, void* out, const void* query, const void* k_
     return PA_ERR_INVALID_ARGUMENT;
   }
   const int64_t parts = split ? max_num_partitions : 1;
-  const int64_t units = int64_t(num_seqs) * num_kv_heads * parts;
+  // Partitions per (sequence, kv head) in the unit grid: all of them, or for
+  // the shared-prefix step's four-wave units a bound on those from each
+  // sequence's first_partition on.
+  const int64_t grid_parts =
+      split && four_wave_units && first_partition && grid_partitions > 0
+          ? (grid_partitions < parts ? grid_partitions : parts)
+          : parts;
+  const int64_t units = int64_t(num_seqs) * num_kv_heads * grid_parts;
   if (units > INT_MAX / 2) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
 
@@ -96,6 +105,7 @@ int decode_impl(DecodeKernel which, void* out, const void* query, const void* k_
   p.scale_log2 = scale * pa::kLog2e;
   p.pages_per_partition = split ? partition_size / PA_PAGE_SIZE : 0;
   p.num_partitions = int(parts);
+  p.grid_partitions = int(grid_parts);
   p.num_units = int(units);
   p.new_key = nullptr;
   p.new_value = nullptr;
@@ -195,10 +205,12 @@ int pa_decode_cascade(const void* query, const void* key, const void* value,
                       int max_pages_per_seq, int64_t num_pages, float scale, int partition_size,
                       int max_num_partitions, float* partial_out, float* partial_max,
                       float* partial_sum, int num_groups, int max_group_size,
-                      int max_group_partitions, const int32_t* group_start,
+                      int max_group_partitions, int max_suffix_partitions,
+                      const int32_t* group_start,
                       const int32_t* group_seqs, const int32_t* group_partitions,
                       const int32_t* seq_first_partition, int dtype, void* stream) {
-  if (partition_size <= 0 || num_groups < 0 || max_group_size < 0 || max_group_partitions < 0)
+  if (partition_size <= 0 || num_groups < 0 || max_group_size < 0 || max_group_partitions < 0 ||
+      max_suffix_partitions < 0)
     return PA_ERR_INVALID_ARGUMENT;
   if (dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;  // matrix-core kernels only
   if (num_groups > 0 && (!group_start || !group_seqs || !group_partitions ||
@@ -251,6 +263,7 @@ int pa_decode_cascade(const void* query, const void* key, const void* value,
     q.num_partitions = max_num_partitions;
     q.max_group_partitions = max_group_partitions;
     q.blocks_per_wave = int(per_wave);
+    q.waves = kPrefixWaves;
     q.column_groups = int(col_groups);
     q.num_units = int(prefix_units);
     if (pa::launch_prefix_partials(q, head_dim, static_cast<hipStream_t>(stream)) != hipSuccess)
@@ -261,7 +274,7 @@ int pa_decode_cascade(const void* query, const void* key, const void* value,
                      max_pages_per_seq, num_pages, scale, partition_size, max_num_partitions,
                      partial_out, partial_max, partial_sum, dtype, stream, key, value,
                      slot_mapping, num_groups > 0 ? seq_first_partition : nullptr,
-                     /*four_wave_units=*/num_groups > 0);
+                     /*four_wave_units=*/num_groups > 0, max_suffix_partitions);
 }
 
 int pa_chunk_attention(void* out, const void* query, const void* k_cache, const void* v_cache,

@@ -32,15 +32,19 @@ struct DecodeParams {
   int64_t num_pages;
   float scale_log2;         // scale * log2(e): scores are kept in base-2 units
   int pages_per_partition;  // 0: the whole context is one unit
-  int num_partitions;       // partitions per (sequence, kv head) in the grid
-  int num_units;            // num_seqs * num_partitions * num_kv_heads
+  int num_partitions;       // partition slots per (sequence, head) row of the partials
+  int grid_partitions;      // partitions per (sequence, kv head) in the unit grid
+  int num_units;            // num_seqs * grid_partitions * num_kv_heads
   // The step's appended token per sequence, written by the decode launch
   // itself (NULL new_key: the caller wrote it with pa_reshape_and_cache).
   const void* new_key;      // [num_seqs][num_kv_heads][head_dim]
   const void* new_value;    // [num_seqs][num_kv_heads][head_dim]
   const int64_t* new_slots; // [num_seqs]; < 0 writes nothing
   // Partitions below first_partition[b] of sequence b are computed elsewhere
-  // (a shared prefix, once per group); NULL: every partition here.
+  // (a shared prefix, once per group); NULL: every partition here.  With
+  // four-wave units the grid's partition index counts from first_partition[b]
+  // (grid_partitions bounds every sequence's remaining partitions), so no
+  // workgroup is spent on a partition computed elsewhere.
   const int32_t* first_partition;
   // Split-KV with four waves per (sequence, partition, kv head) unit instead
   // of one: for batches with few units for the machine.
@@ -75,6 +79,7 @@ struct PrefixParams {
   int num_partitions;               // partition slots per row of the partial arrays
   int max_group_partitions;         // grid bound
   int blocks_per_wave;              // 16-column blocks a wave carries (1 or 2)
+  int waves;                        // waves per unit (4 or 8), splitting a partition's pages
   int column_groups;                // ceil(max members * group / (16 * blocks_per_wave))
   int num_units;
 };
@@ -118,8 +123,8 @@ __device__ inline bool unit_of_block(const DecodeParams& p, int& seq, int& kvh, 
   if (u >= p.num_units) return false;
   kvh = u % p.num_kv_heads;
   const int rest = u / p.num_kv_heads;
-  part = rest % p.num_partitions;
-  seq = rest / p.num_partitions;
+  part = rest % p.grid_partitions;
+  seq = rest / p.grid_partitions;
   return true;
 }
 
@@ -154,16 +159,24 @@ template <> struct Elem<uint16_t> {
   }
 };
 
+// Rows of accumulators merged through LDS are head_dim + kAccPad floats
+// apart.  A matrix-core lane holds four consecutive dims of one column and
+// writes them as one 16-byte store; with unpadded rows the 16 columns' lanes
+// of a store would all hit the same banks (a 16-way conflict), with the pad
+// they cover all 64 banks.
+constexpr int kAccPad = 4;
+
 // LDS used by the merge: per wave a reference max and a sum per head, and
 // the un-normalised accumulator [wave][head][dim] for the group's heads.
 __host__ __device__ inline size_t merge_lds_bytes(int group, int head_dim) {
-  return sizeof(float) * (2 * kWaves * kMaxGroup + size_t(kWaves) * group * head_dim);
+  return sizeof(float) *
+         (2 * kWaves * kMaxGroup + size_t(kWaves) * group * (head_dim + kAccPad));
 }
 
 struct MergeLds {
   float* m;    // [kWaves][kMaxGroup]  base-2 reference score
   float* l;    // [kWaves][kMaxGroup]  sum of 2^(s - m)
-  float* acc;  // [kWaves][group][D]
+  float* acc;  // [kWaves][group][D + kAccPad]
   __device__ MergeLds(float* smem) : m(smem), l(smem + kWaves * kMaxGroup),
                                      acc(smem + 2 * kWaves * kMaxGroup) {}
 };
@@ -188,7 +201,7 @@ __device__ inline void merge_and_store(const DecodeParams& p, const MergeLds& s,
       const float mw = s.m[w * kMaxGroup + h];
       const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
       wsum += s.l[w * kMaxGroup + h] * f;
-      num += s.acc[(w * G + h) * D + d] * f;
+      num += s.acc[(w * G + h) * (D + kAccPad) + d] * f;
     }
     const float o = wsum > 0.f ? num / wsum : 0.f;
     const int qh = kvh * G + h;

@@ -326,9 +326,10 @@ int pa_pager_prefix_groups(const int32_t* block_tables, const int32_t* context_l
                            int64_t num_seqs, int max_pages_per_seq, int pages_per_partition,
                            int32_t* group_start, int32_t* group_seqs, int32_t* group_partitions,
                            int32_t* seq_first_partition, int64_t* num_groups,
-                           int64_t* max_group_size, int64_t* max_group_partitions) {
+                           int64_t* max_group_size, int64_t* max_group_partitions,
+                           int64_t* max_suffix_partitions) {
   if (num_seqs < 0 || max_pages_per_seq <= 0 || pages_per_partition <= 0 || !num_groups ||
-      !max_group_size || !max_group_partitions || !group_start)
+      !max_group_size || !max_group_partitions || !max_suffix_partitions || !group_start)
     return PA_PAGER_INVALID_ARGUMENT;
   if (num_seqs > 0 && (!block_tables || !context_lens || !group_seqs || !group_partitions ||
                        !seq_first_partition))
@@ -377,9 +378,17 @@ int pa_pager_prefix_groups(const int32_t* block_tables, const int32_t* context_l
     max_size = std::max<int64_t>(max_size, int64_t(members.size()));
     max_parts = std::max<int64_t>(max_parts, parts);
   }
+  int64_t max_suffix = 0;
+  for (int64_t b = 0; b < num_seqs; ++b) {
+    const int64_t L = std::max(context_lens[b], 0);
+    const int64_t pages = std::min<int64_t>((L + P - 1) / P, max_pages_per_seq);
+    const int64_t parts = (pages + pages_per_partition - 1) / pages_per_partition;
+    max_suffix = std::max(max_suffix, parts - seq_first_partition[b]);
+  }
   *num_groups = g;
   *max_group_size = max_size;
   *max_group_partitions = max_parts;
+  *max_suffix_partitions = max_suffix;
   return PA_PAGER_OK;
 }
 

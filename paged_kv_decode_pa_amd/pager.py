@@ -61,7 +61,7 @@ def load(path: str = PAGER_LIB_PATH) -> ctypes.CDLL:
         "pa_pager_drain_events": ([_P, _I32P, _I64P, _U64P, ctypes.c_int64, _I64P], ctypes.c_int),
         "pa_pager_page_hash": ([ctypes.c_uint64, _I32P, ctypes.c_int], ctypes.c_uint64),
         "pa_pager_prefix_groups": ([_I32P, _I32P, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
-                                    _I32P, _I32P, _I32P, _I32P, _I64P, _I64P, _I64P],
+                                    _I32P, _I32P, _I32P, _I32P, _I64P, _I64P, _I64P, _I64P],
                                    ctypes.c_int),
     }
     for name, (args, res) in sig.items():
@@ -91,14 +91,16 @@ def prefix_groups(block_tables, context_lens, pages_per_partition: int) -> dict:
     seqs = np.zeros(max(B, 1), dtype=np.int32)
     parts = np.zeros(max(B, 1), dtype=np.int32)
     first = np.zeros(max(B, 1), dtype=np.int32)
-    ng, mg, mp = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    ng, mg, mp, ms = (ctypes.c_int64() for _ in range(4))
     st = load().pa_pager_prefix_groups(
         _ptr(bt), _ptr(lens), B, max_pages, int(pages_per_partition), _ptr(start), _ptr(seqs),
-        _ptr(parts), _ptr(first), ctypes.byref(ng), ctypes.byref(mg), ctypes.byref(mp))
+        _ptr(parts), _ptr(first), ctypes.byref(ng), ctypes.byref(mg), ctypes.byref(mp),
+        ctypes.byref(ms))
     if st != OK:
         raise PagerError("pa_pager_prefix_groups", st)
     n = ng.value
     return {"num_groups": n, "max_group_size": mg.value, "max_group_partitions": mp.value,
+            "max_suffix_partitions": ms.value,
             "group_start": start[:n + 1].copy(), "group_seqs": seqs[:start[n]].copy(),
             "group_partitions": parts[:n].copy(), "seq_first_partition": first[:B].copy()}
 

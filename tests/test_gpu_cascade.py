@@ -116,3 +116,19 @@ def test_out_of_range_members_are_skipped():
     bad = dict(g, group_start=s, group_seqs=seqs, max_group_size=g["max_group_size"] + 2)
     got = cascade(DeviceWorkload(wl), 512, bad)
     assert np.array_equal(bits_of(got), bits_of(want))
+
+
+@pytest.mark.parametrize("ps", [256, 1024])
+def test_suffix_grid_bound(ps):
+    """The second launch's grid counts each sequence's partitions from its
+    first: the tight bound from prefix_groups, a looser one and none (0) give
+    the same bits."""
+    say(f"[cascade] suffix grid bound, partition {ps}")
+    wl = config_workload(3)
+    g = pa.prefix_groups(wl.block_tables, wl.context_lens, ps // 16)
+    dev = DeviceWorkload(wl)
+    tight = bits_of(cascade(dev, ps, g))
+    assert g["max_suffix_partitions"] >= 1
+    for bound in (0, g["max_suffix_partitions"] + 2):
+        assert np.array_equal(bits_of(cascade(dev, ps, dict(g, max_suffix_partitions=bound))), tight)
+    assert float(np.abs(f64_of(cascade(dev, ps, g)) - oracle_reference(wl)).max()) <= TOL["bf16"]

@@ -334,3 +334,5 @@ def test_prefix_groups_match_the_rule(seed):
     assert got["seq_first_partition"].tolist() == first
     assert got["max_group_size"] == max([len(m) for m, _ in groups], default=0)
     assert got["max_group_partitions"] == max([p for _, p in groups], default=0)
+    parts = [-(-min(-(-int(L) // 16), max_pages) // pp) for L in lens]
+    assert got["max_suffix_partitions"] == max(parts[b] - first[b] for b in range(B))
