@@ -229,12 +229,12 @@ int pa_decode_append(void* out, const void* query, const void* key, const void* 
  * those pages lies inside every member's context.  For each such partition and
  * kv head one work unit reads the pages once and computes every member's
  * partial for it: the members' query heads are the columns of the matrix
- * tiles, up to 32 per wave.  Then a second launch computes each sequence's
- * partitions from seq_first_partition[b] on (0 for sequences in no group),
- * four waves per (sequence, partition, kv head).  With key/value/slot_mapping
- * non-NULL that launch also writes the step's new token, as pa_decode_append
- * does.  The partial arrays end up as pa_decode (split) writes them: merge
- * them with pa_decode_reduce.
+ * tiles, up to 32 per wave.  In the same launch, units of four waves per
+ * (sequence, partition, kv head) compute each sequence's partitions from
+ * seq_first_partition[b] on (0 for sequences in no group).  With
+ * key/value/slot_mapping non-NULL those units also write the step's new
+ * token, as pa_decode_append does.  The partial arrays end up as pa_decode
+ * (split) writes them: merge them with pa_decode_reduce.
  *
  *   num_groups, max_group_size, max_group_partitions  host bounds that size
  *               the grid: groups of more members or partitions are not fully
@@ -242,8 +242,8 @@ int pa_decode_append(void* out, const void* query, const void* key, const void* 
  *               not exceed max_num_partitions.
  *   max_suffix_partitions  host bound on min(ceil(L_b / partition_size),
  *               max_num_partitions) - seq_first_partition[b] over the batch:
- *               the second launch's grid holds that many partitions per
- *               sequence, counted from its first.  A smaller value than the
+ *               the grid holds that many partitions per sequence, counted
+ *               from its first.  A smaller value than the
  *               true maximum leaves partitions uncomputed (unspecified
  *               results); 0 means max_num_partitions (always enough, at the
  *               cost of workgroups that find nothing to do).

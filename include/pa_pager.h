@@ -143,7 +143,7 @@ int pa_pager_drain_events(pa_pager* pager, int32_t* kinds, int64_t* pages, uint6
  * *max_group_partitions, and *max_suffix_partitions: the most partitions any
  * sequence has from its seq_first_partition on (ceil(min(ceil(L / 16),
  * max_pages_per_seq) / pages_per_partition) - first), the bound
- * pa_decode_cascade sizes its second launch by. */
+ * pa_decode_cascade sizes its grid by. */
 int pa_pager_prefix_groups(const int32_t* block_tables, const int32_t* context_lens,
                            int64_t num_seqs, int max_pages_per_seq, int pages_per_partition,
                            int32_t* group_start, int32_t* group_seqs, int32_t* group_partitions,

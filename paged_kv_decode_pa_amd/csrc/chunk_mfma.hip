@@ -20,7 +20,7 @@
 // same pages, and the kv-head-fastest unit order puts them on one XCD's L2.
 #include <limits.h>
 
-#include "page_stream.hpp"
+#include "wave_attn.hpp"
 
 namespace pa {
 namespace {
@@ -324,17 +324,13 @@ __global__ __launch_bounds__(kBlock) void chunk_attention_kernel(ChunkParams p) 
 }
 
 // Shared-prefix partials.  Unit = (group, shared partition, column group,
-// kv head), W waves; wave w takes the partition's pages w, w+W, ... from the
-// first member's block-table row (the members hold the same page ids there).
-// Column c of the unit's blocks is member c / group, query head c % group of
-// the kv head.  Eight waves halve each wave's chain of dependent page steps
-// against four: the pass has few units (groups x shared partitions), and its
-// time is those chains.
-template <int D, int NB, int W>
-__global__ __launch_bounds__(64 * W) void prefix_partial_kernel(PrefixParams p) {
-  extern __shared__ float smem[];
-  const int u = blockIdx.x;
-  if (u >= p.num_units) return;
+// kv head), four waves; wave w takes the partition's pages w, w+4, ... from
+// the first member's block-table row (the members hold the same page ids
+// there).  Column c of the unit's blocks is member c / group, query head
+// c % group of the kv head.  (Eight waves per unit, each walking half the
+// pages, measured slower.)
+template <int D, int NB>
+__device__ inline void prefix_unit(const PrefixParams& p, int u, float* smem) {
   const int kvh = u % p.num_kv_heads;
   int rest = u / p.num_kv_heads;
   const int cg = rest % p.column_groups;
@@ -360,7 +356,7 @@ __global__ __launch_bounds__(64 * W) void prefix_partial_kernel(PrefixParams p) 
   PageStream<D> ps;
   ps.table = p.block_tables + size_t(first_seq) * p.max_pages_per_seq;
   ps.first = lo + w;
-  ps.step = W;
+  ps.step = kWaves;
   ps.row_end = hi;
   ps.kpool = static_cast<const char*>(p.k_cache);
   ps.vpool = static_cast<const char*>(p.v_cache);
@@ -370,7 +366,7 @@ __global__ __launch_bounds__(64 * W) void prefix_partial_kernel(PrefixParams p) 
   ps.koff = uint32_t(r * D + 8 * j) * 2u;
   ps.voff = uint32_t(r * kPage + 4 * j) * 2u;
   ps.start(lane);
-  ps.count = lo + w < hi ? (hi - lo - w + W - 1) / W : 0;
+  ps.count = lo + w < hi ? (hi - lo - w + kWaves - 1) / kWaves : 0;
 
   ColumnAttn<D> wa[NB];
   int col_seq[NB];  // batch index of column r's member, -1 for no member
@@ -388,13 +384,13 @@ __global__ __launch_bounds__(64 * W) void prefix_partial_kernel(PrefixParams p) 
   }
   run_clear<D, NB>(wa, ps, lo + w, lane);
 
-  // Merge the W waves per column and write each member's partial for this
+  // Merge the four waves per column and write each member's partial for this
   // partition, one block at a time through the same LDS.  The columns'
   // members go to LDS once, so the stores wait on no global load.
-  float* lm = smem;                 // [W][16]
-  float* ll = smem + W * 16;        // [W][16]
-  float* la = smem + 2 * W * 16;    // [W][16][D + kAccPad]
-  int* lseq = reinterpret_cast<int*>(la + W * 16 * (D + kAccPad));  // [NB][16]
+  float* lm = smem;                 // [kWaves][16]
+  float* ll = smem + kWaves * 16;        // [kWaves][16]
+  float* la = smem + 2 * kWaves * 16;    // [kWaves][16][D + kAccPad]
+  int* lseq = reinterpret_cast<int*>(la + kWaves * 16 * (D + kAccPad));  // [NB][16]
   if (w == 0 && j == 0) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) lseq[nb * 16 + r] = col_seq[nb];
@@ -414,7 +410,7 @@ __global__ __launch_bounds__(64 * W) void prefix_partial_kernel(PrefixParams p) 
           wa[nb].acc[db];
     __syncthreads();
     // Thread: one column's four consecutive dims per step.
-    for (int idx = threadIdx.x; idx < 16 * (D / 4); idx += 64 * W) {
+    for (int idx = threadIdx.x; idx < 16 * (D / 4); idx += kBlock) {
       const int col = idx / (D / 4);
       const int d = 4 * (idx % (D / 4));
       const int cc = c_lo + col;
@@ -422,11 +418,11 @@ __global__ __launch_bounds__(64 * W) void prefix_partial_kernel(PrefixParams p) 
       if (cc >= cols || seq < 0) continue;
       float M = -INFINITY;
 #pragma unroll
-      for (int v = 0; v < W; ++v) M = fmaxf(M, lm[v * 16 + col]);
+      for (int v = 0; v < kWaves; ++v) M = fmaxf(M, lm[v * 16 + col]);
       float wsum = 0.f;
       f32x4 num = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int v = 0; v < W; ++v) {
+      for (int v = 0; v < kWaves; ++v) {
         const float mv = lm[v * 16 + col];
         const float f = mv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv - M);
         wsum += ll[v * 16 + col] * f;
@@ -448,6 +444,26 @@ __global__ __launch_bounds__(64 * W) void prefix_partial_kernel(PrefixParams p) 
   }
 }
 
+// The shared-prefix step in one launch: blocks below q.num_units are the
+// prefix units (the longest, dispatched first), the rest the four-wave
+// split-KV units of every sequence's own partitions.  The two sets write
+// disjoint partials and touch disjoint pages (a page that receives the
+// step's token is never shared), so they need no ordering; in one grid the
+// suffix units fill the machine while the prefix units stream, and each
+// set's setup and merge phases overlap the other's page loads.
+template <int D, int NB>
+__global__ __launch_bounds__(kBlock) void cascade_kernel(PrefixParams q, DecodeParams p) {
+  extern __shared__ float smem[];
+  const int b = blockIdx.x;
+  if (b < q.num_units) {
+    prefix_unit<D, NB>(q, b, smem);
+    return;
+  }
+  int seq, kvh, part;
+  if (!unit_of(p, b - q.num_units, seq, kvh, part)) return;
+  whole_unit<D>(p, seq, kvh, part, smem);
+}
+
 template <int D>
 void launch_d(const ChunkParams& p, size_t lds, hipStream_t stream) {
   const dim3 grid(p.num_units);
@@ -461,22 +477,20 @@ void launch_d(const ChunkParams& p, size_t lds, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_prefix_partials(const PrefixParams& p, int head_dim, hipStream_t stream) {
-  const dim3 grid(p.num_units);
-  const int W = p.waves;
-  const size_t lds = sizeof(float) * (2 * W * 16 + size_t(W) * 16 * (head_dim + kAccPad)) +
-                     sizeof(int) * 2 * 16;  // + the columns' members, two blocks at most
-#define PA_PREFIX(DD, NBB, WW) \
-  prefix_partial_kernel<DD, NBB, WW><<<grid, 64 * WW, lds, stream>>>(p)
-#define PA_PREFIX_W(DD, NBB) \
-  do { if (W == 8) PA_PREFIX(DD, NBB, 8); else PA_PREFIX(DD, NBB, 4); } while (0)
+hipError_t launch_cascade(const PrefixParams& q, const DecodeParams& p, int head_dim,
+                          hipStream_t stream) {
+  const size_t prefix_lds = sizeof(float) * (2 * kWaves * 16 + size_t(kWaves) * 16 *
+                                             (head_dim + kAccPad)) + sizeof(int) * 2 * 16;
+  const size_t suffix_lds = merge_lds_bytes(p.group, head_dim);
+  const size_t lds = prefix_lds > suffix_lds ? prefix_lds : suffix_lds;
+  const dim3 grid(q.num_units + p.num_units);
+#define PA_CASCADE(DD, NBB) cascade_kernel<DD, NBB><<<grid, kBlock, lds, stream>>>(q, p)
   if (head_dim == 128) {
-    if (p.blocks_per_wave == 1) PA_PREFIX_W(128, 1); else PA_PREFIX_W(128, 2);
+    if (q.blocks_per_wave == 1) PA_CASCADE(128, 1); else PA_CASCADE(128, 2);
   } else {
-    if (p.blocks_per_wave == 1) PA_PREFIX_W(64, 1); else PA_PREFIX_W(64, 2);
+    if (q.blocks_per_wave == 1) PA_CASCADE(64, 1); else PA_CASCADE(64, 2);
   }
-#undef PA_PREFIX_W
-#undef PA_PREFIX
+#undef PA_CASCADE
   return hipGetLastError();
 }
 

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(kBlock) void decode_valu_kernel(DecodeParams p) {
   constexpr int QD = D / 4;    // key dims per lane
   constexpr int VD = D / 64;   // value dims per lane
   int seq, kvh, part;
-  if (!unit_of_block(p, seq, kvh, part)) return;
+  if (!unit_of(p, blockIdx.x, seq, kvh, part)) return;
   const int L = p.context_lens[seq];
   int lo, hi;
   if (!unit_pages(p, seq, part, L, lo, hi)) {

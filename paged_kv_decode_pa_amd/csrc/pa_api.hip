@@ -15,7 +15,8 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
                                     int num_kv_heads, int head_dim, int64_t num_pages, bool bf16,
                                     hipStream_t stream);
 hipError_t launch_chunk_attention(const ChunkParams& p, int head_dim, hipStream_t stream);
-hipError_t launch_prefix_partials(const PrefixParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_cascade(const PrefixParams& q, const DecodeParams& p, int head_dim,
+                          hipStream_t stream);
 hipError_t launch_page_copy(bool export_dir, void* buf, void* k_cache, void* v_cache,
                             const int32_t* page_ids, int64_t num_ids, int64_t num_pages,
                             int64_t block_bytes, hipStream_t stream);
@@ -28,7 +29,6 @@ hipError_t launch_decode_reduce(void* out, const float* part_out, const float* p
 namespace {
 
 constexpr int kVersion = 10000;  // 1.0.0
-constexpr int kPrefixWaves = 4;  // waves per shared-prefix unit
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -41,18 +41,19 @@ int check_common(int head_dim, int page_size, int dtype) {
 
 enum class DecodeKernel { kAuto, kValu };
 
-// new_key == NULL: decode only.  Otherwise the launch first writes each
-// sequence's new token (new_key/new_value rows, slot new_slots[b]): inside the
-// matrix-core kernels, or as a separate cache-write launch for the others.
-int decode_impl(DecodeKernel which, void* out, const void* query, const void* k_cache,
-                const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
-                int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int page_size,
-                int max_pages_per_seq, int64_t num_pages, float scale, int partition_size,
-                int max_num_partitions, float* partial_out, float* partial_max,
-                float* partial_sum, int dtype, void* stream, const void* new_key = nullptr,
-                const void* new_value = nullptr, const int64_t* new_slots = nullptr,
-                const int32_t* first_partition = nullptr, bool four_wave_units = false,
-                int grid_partitions = 0) {
+// Checks a decode call's host arguments and fills its launch parameters;
+// *empty when there is nothing to launch.  new_key == NULL: decode only.
+// Otherwise the launch first writes each sequence's new token (new_key /
+// new_value rows, slot new_slots[b]): inside the matrix-core kernels (*fused),
+// or as a separate cache-write launch for the others.
+int decode_setup(DecodeKernel which, void* out, const void* query, const void* k_cache,
+                 const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                 int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                 int max_pages_per_seq, int64_t num_pages, float scale, int partition_size,
+                 int max_num_partitions, float* partial_out, float* partial_max,
+                 float* partial_sum, int dtype, const void* new_key, const void* new_value,
+                 const int64_t* new_slots, const int32_t* first_partition, bool four_wave_units,
+                 int grid_partitions, pa::DecodeParams& p, bool& mfma, bool& empty) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_pages_per_seq <= 0 ||
       num_pages <= 0 || partition_size < 0)
     return PA_ERR_INVALID_ARGUMENT;
@@ -84,9 +85,8 @@ int decode_impl(DecodeKernel which, void* out, const void* query, const void* k_
           : parts;
   const int64_t units = int64_t(num_seqs) * num_kv_heads * grid_parts;
   if (units > INT_MAX / 2) return PA_ERR_UNSUPPORTED;
-  if (num_seqs == 0) return PA_OK;
+  empty = num_seqs == 0;
 
-  pa::DecodeParams p;
   p.out = out;
   p.query = query;
   p.k_cache = k_cache;
@@ -107,19 +107,34 @@ int decode_impl(DecodeKernel which, void* out, const void* query, const void* k_
   p.num_partitions = int(parts);
   p.grid_partitions = int(grid_parts);
   p.num_units = int(units);
-  p.new_key = nullptr;
-  p.new_value = nullptr;
-  p.new_slots = nullptr;
   p.first_partition = first_partition;
   p.four_wave_units = four_wave_units && split;
+  mfma = dtype == PA_DTYPE_BF16 && which == DecodeKernel::kAuto;
+  p.new_key = mfma ? new_key : nullptr;
+  p.new_value = mfma ? new_value : nullptr;
+  p.new_slots = mfma ? new_slots : nullptr;
+  return PA_OK;
+}
+
+int decode_impl(DecodeKernel which, void* out, const void* query, const void* k_cache,
+                const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                int max_pages_per_seq, int64_t num_pages, float scale, int partition_size,
+                int max_num_partitions, float* partial_out, float* partial_max,
+                float* partial_sum, int dtype, void* stream, const void* new_key = nullptr,
+                const void* new_value = nullptr, const int64_t* new_slots = nullptr) {
+  pa::DecodeParams p;
+  bool mfma = false, empty = false;
+  if (int st = decode_setup(which, out, query, k_cache, v_cache, block_tables, context_lens,
+                            num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
+                            max_pages_per_seq, num_pages, scale, partition_size,
+                            max_num_partitions, partial_out, partial_max, partial_sum, dtype,
+                            new_key, new_value, new_slots, nullptr, false, 0, p, mfma, empty))
+    return st;
+  if (empty) return PA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = dtype == PA_DTYPE_BF16;
-  const bool mfma = bf16 && which == DecodeKernel::kAuto;
-  if (new_key && mfma) {
-    p.new_key = new_key;
-    p.new_value = new_value;
-    p.new_slots = new_slots;
-  } else if (new_key) {
+  if (new_key && !mfma) {
     const hipError_t e = pa::launch_reshape_and_cache(new_key, new_value, const_cast<void*>(k_cache),
                                                       const_cast<void*>(v_cache), new_slots,
                                                       num_seqs, num_kv_heads, head_dim, num_pages,
@@ -218,63 +233,59 @@ int pa_decode_cascade(const void* query, const void* key, const void* value,
     return PA_ERR_INVALID_ARGUMENT;
   if ((key != nullptr) != (value != nullptr) || (key != nullptr) != (slot_mapping != nullptr))
     return PA_ERR_INVALID_ARGUMENT;
-  // The decode's own checks are repeated here so that a bad argument
-  // launches nothing (the prefix kernel goes first).
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
     return PA_ERR_INVALID_ARGUMENT;
-  if (int s = check_common(head_dim, page_size, dtype)) return s;
+  pa::DecodeParams p;
+  bool mfma = false, empty = false;
+  if (int st = decode_setup(DecodeKernel::kAuto, nullptr, query, k_cache, v_cache, block_tables,
+                            context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                            page_size, max_pages_per_seq, num_pages, scale, partition_size,
+                            max_num_partitions, partial_out, partial_max, partial_sum, dtype, key,
+                            value, slot_mapping, num_groups > 0 ? seq_first_partition : nullptr,
+                            /*four_wave_units=*/num_groups > 0, max_suffix_partitions, p, mfma,
+                            empty))
+    return st;
   const int group = num_q_heads / num_kv_heads;
-  if (group > PA_MAX_GQA_GROUP) return PA_ERR_UNSUPPORTED;
-  if (num_pages <= 0 || max_pages_per_seq <= 0 || num_seqs < 0 || max_num_partitions < 1 ||
-      partition_size % PA_PAGE_SIZE != 0 || !query || !k_cache || !v_cache || !block_tables ||
-      !context_lens || !partial_out || !partial_max || !partial_sum || !aligned16(query) ||
-      !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(partial_out) || !isfinite(scale))
-    return PA_ERR_INVALID_ARGUMENT;
   // At most two 16-column blocks per wave (202 VGPRs, two waves per SIMD):
-  // measured faster here than four blocks at one wave per SIMD.
+  // measured faster here than four blocks at one wave per SIMD, and than
+  // one block (146 VGPRs, three waves per SIMD).
   const int64_t blocks = (int64_t(max_group_size) * group + 15) / 16;
   const int64_t per_wave = blocks < 2 ? (blocks > 0 ? blocks : 1) : 2;
   const int64_t col_groups = (blocks + per_wave - 1) / per_wave;
   const int64_t prefix_units =
       int64_t(num_groups) * max_group_partitions * col_groups * num_kv_heads;
-  if (prefix_units > INT_MAX / 2) return PA_ERR_UNSUPPORTED;
-  if (num_seqs == 0) return PA_OK;
-  if (prefix_units > 0) {
-    pa::PrefixParams q;
-    q.query = query;
-    q.k_cache = k_cache;
-    q.v_cache = v_cache;
-    q.block_tables = block_tables;
-    q.partial_out = partial_out;
-    q.partial_max = partial_max;
-    q.partial_sum = partial_sum;
-    q.group_start = group_start;
-    q.group_seqs = group_seqs;
-    q.group_partitions = group_partitions;
-    q.num_groups = num_groups;
-    q.num_seqs = num_seqs;
-    q.num_q_heads = num_q_heads;
-    q.num_kv_heads = num_kv_heads;
-    q.group = group;
-    q.max_pages_per_seq = max_pages_per_seq;
-    q.num_pages = num_pages;
-    q.scale_log2 = scale * pa::kLog2e;
-    q.pages_per_partition = partition_size / PA_PAGE_SIZE;
-    q.num_partitions = max_num_partitions;
-    q.max_group_partitions = max_group_partitions;
-    q.blocks_per_wave = int(per_wave);
-    q.waves = kPrefixWaves;
-    q.column_groups = int(col_groups);
-    q.num_units = int(prefix_units);
-    if (pa::launch_prefix_partials(q, head_dim, static_cast<hipStream_t>(stream)) != hipSuccess)
-      return PA_ERR_LAUNCH;
-  }
-  return decode_impl(DecodeKernel::kAuto, nullptr, query, k_cache, v_cache, block_tables,
-                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
-                     max_pages_per_seq, num_pages, scale, partition_size, max_num_partitions,
-                     partial_out, partial_max, partial_sum, dtype, stream, key, value,
-                     slot_mapping, num_groups > 0 ? seq_first_partition : nullptr,
-                     /*four_wave_units=*/num_groups > 0, max_suffix_partitions);
+  if (prefix_units > INT_MAX / 2 || prefix_units + p.num_units > INT_MAX / 2)
+    return PA_ERR_UNSUPPORTED;
+  if (empty) return PA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (prefix_units == 0)
+    return pa::launch_decode_mfma(p, head_dim, s) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+  pa::PrefixParams q;
+  q.query = query;
+  q.k_cache = k_cache;
+  q.v_cache = v_cache;
+  q.block_tables = block_tables;
+  q.partial_out = partial_out;
+  q.partial_max = partial_max;
+  q.partial_sum = partial_sum;
+  q.group_start = group_start;
+  q.group_seqs = group_seqs;
+  q.group_partitions = group_partitions;
+  q.num_groups = num_groups;
+  q.num_seqs = num_seqs;
+  q.num_q_heads = num_q_heads;
+  q.num_kv_heads = num_kv_heads;
+  q.group = group;
+  q.max_pages_per_seq = max_pages_per_seq;
+  q.num_pages = num_pages;
+  q.scale_log2 = scale * pa::kLog2e;
+  q.pages_per_partition = partition_size / PA_PAGE_SIZE;
+  q.num_partitions = max_num_partitions;
+  q.max_group_partitions = max_group_partitions;
+  q.blocks_per_wave = int(per_wave);
+  q.column_groups = int(col_groups);
+  q.num_units = int(prefix_units);
+  return pa::launch_cascade(q, p, head_dim, s) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 int pa_chunk_attention(void* out, const void* query, const void* k_cache, const void* v_cache,

@@ -79,7 +79,6 @@ struct PrefixParams {
   int num_partitions;               // partition slots per row of the partial arrays
   int max_group_partitions;         // grid bound
   int blocks_per_wave;              // 16-column blocks a wave carries (1 or 2)
-  int waves;                        // waves per unit (4 or 8), splitting a partition's pages
   int column_groups;                // ceil(max members * group / (16 * blocks_per_wave))
   int num_units;
 };
@@ -117,14 +116,16 @@ __host__ __device__ inline int decode_grid(int num_units) { return num_units; }
 // fastest.  Workgroups are dispatched round-robin over the 8 XCDs (block b
 // runs on XCD b % 8), so with 8 kv heads (or a multiple) each XCD owns whole
 // kv heads: every XCD gets the same share of every sequence, and all the
-// sequences that share a prefix page read it through one XCD's L2.
-__device__ inline bool unit_of_block(const DecodeParams& p, int& seq, int& kvh, int& part) {
-  const int u = blockIdx.x;
+// sequences that share a prefix page read it through one XCD's L2.  With
+// first_partition the partition index counts from the sequence's first.
+__device__ inline bool unit_of(const DecodeParams& p, int u, int& seq, int& kvh, int& part) {
   if (u >= p.num_units) return false;
   kvh = u % p.num_kv_heads;
   const int rest = u / p.num_kv_heads;
   part = rest % p.grid_partitions;
   seq = rest / p.grid_partitions;
+  if (p.first_partition)  // partitions below it are computed elsewhere
+    part += min(max(p.first_partition[seq], 0), p.num_partitions);
   return true;
 }
 

@@ -1,5 +1,5 @@
-"""pa_decode_cascade: shared prefix partitions read once per group, then the
-split-KV kernel over each sequence's own partitions, merged by
+"""pa_decode_cascade: shared prefix partitions read once per group and the
+split-KV units of each sequence's own partitions, in one launch, merged by
 pa_decode_reduce.  Checked against the oracle, against the plain split
 decode, for determinism, with the step's token written in the same call, and
 with groups that span several column groups or hold out-of-range members."""
@@ -120,7 +120,7 @@ def test_out_of_range_members_are_skipped():
 
 @pytest.mark.parametrize("ps", [256, 1024])
 def test_suffix_grid_bound(ps):
-    """The second launch's grid counts each sequence's partitions from its
+    """The suffix units' grid counts each sequence's partitions from its
     first: the tight bound from prefix_groups, a looser one and none (0) give
     the same bits."""
     say(f"[cascade] suffix grid bound, partition {ps}")
