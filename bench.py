@@ -35,9 +35,11 @@ METRIC = "paged decode attention: achieved KV HBM GB/s (% of peak) + seqs/sec, 1
 PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, vendor peak
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["paged_kv_decode_pa_amd/csrc/decode_mfma.hip",
+                  "paged_kv_decode_pa_amd/csrc/wave_attn.hpp",
                   "paged_kv_decode_pa_amd/csrc/page_stream.hpp",
                   "paged_kv_decode_pa_amd/csrc/pa_device.hpp"]
 CHUNK_KERNEL_SOURCES = ["paged_kv_decode_pa_amd/csrc/chunk_mfma.hip",
+                        "paged_kv_decode_pa_amd/csrc/wave_attn.hpp",
                         "paged_kv_decode_pa_amd/csrc/page_stream.hpp",
                         "paged_kv_decode_pa_amd/csrc/pa_device.hpp"]
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
@@ -74,7 +76,11 @@ def parse_args():
                     help="auto = pa_decode; valu = pa_decode_valu")
     ap.add_argument("--cascade", action="store_true",
                     help="read pages shared by a group of sequences once per group "
-                         "(pa_decode_cascade; split-KV only)")
+                         "(pa_decode_cascade; split-KV only; the prefix-reuse workload's "
+                         "default)")
+    ap.add_argument("--no-cascade", action="store_true",
+                    help="the prefix-reuse workload without pa_decode_cascade (every "
+                         "sequence reads its own block-table row)")
     ap.add_argument("--unfused", action="store_true",
                     help="time the step as three calls (pa_reshape_and_cache, pa_decode, reduce) "
                          "instead of pa_decode_append + reduce")
@@ -152,10 +158,11 @@ def read_profile_kv(name, sources):
     return kv
 
 
-def read_traffic(cid, partition_size):
+def read_traffic(cid, partition_size, cascade=False):
     """HBM bytes per decode launch from a committed counter summary, or None
     when the summary is absent or the kernel changed since it was taken."""
-    kv = read_profile_kv(f"traffic_decode_mfma_cfg{cid}.txt", KERNEL_SOURCES)
+    kv = (read_profile_kv(f"traffic_cascade_cfg{cid}.txt", CHUNK_KERNEL_SOURCES) if cascade else
+          read_profile_kv(f"traffic_decode_mfma_cfg{cid}.txt", KERNEL_SOURCES))
     if kv is None or int(kv.get("partition_size", -1)) != partition_size:
         return None
     try:
@@ -182,7 +189,9 @@ def run_config(cid, args, headline):
     from workloads import config_by_id, make_workload
 
     cfg = config_by_id(cid)
-    ps = cfg.bench_partition_size if args.partition_size is None else args.partition_size
+    cascade = (args.cascade or cfg.bench_cascade) and not (args.no_cascade or args.unshared)
+    default_ps = cfg.cascade_partition_size if cascade and cfg.bench_cascade else cfg.bench_partition_size
+    ps = default_ps if args.partition_size is None else args.partition_size
     t0 = time.time()
     wl = make_workload(cfg, share_prefix=not args.unshared)
     print(f"[bench] config {cid} ({cfg.name}{', unshared' if args.unshared else ''}) drawn in {time.time() - t0:.1f}s; "
@@ -223,7 +232,7 @@ def run_config(cid, args, headline):
     # unless --unfused or the vector kernel is asked for.
     fused = args.kernel == "auto" and not args.unfused
     groups = None
-    if args.cascade:
+    if cascade:
         if not ps or wl.dtype != "bf16" or args.kernel != "auto":
             raise SystemExit("--cascade needs a bf16 workload, the matrix-core kernels and a "
                              "partition size")
@@ -333,6 +342,16 @@ def run_config(cid, args, headline):
         copy_calibration(dev)
 
     nb = byte_counts(wl, ps)
+    if groups is not None and int(groups["num_groups"]) > 0:
+        # the prefix units carry one or two 16-column blocks per wave
+        blocks = -(-int(groups["max_group_size"]) * (Hq // Hkv) // 16)
+        roof_kernel = f"cascade_kernel<{D}, {min(max(blocks, 1), 2)}>"
+        traffic = read_traffic(cid, ps, cascade=True)
+    else:
+        roof_kernel = ("decode_valu_kernel" if (wl.dtype != "bf16" or args.kernel != "auto")
+                       else "decode_split_kernel" if ps else "decode_whole_kernel") + f"<{D}>"
+        traffic = (read_traffic(cid, ps) if (wl.dtype == "bf16" and args.kernel == "auto")
+                   else None)
     t_step = float(np.mean(step_ms)) * 1e-3
     t_dec = float(np.mean(decode_ms)) * 1e-3
     gbs = nb["kv_unique"] / t_step / 1e9
@@ -354,8 +373,13 @@ def run_config(cid, args, headline):
         "config": {
             "workload": WORKLOAD_NAMES[cid],
             "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "page_size": P,
-            "partition_size": ps, "prefix_pages_shared": not args.unshared, "kernel": ("pa_decode_append (cache write inside the decode launch)" if fused else
-                       "pa_decode" if args.kernel == "auto" else "pa_decode_valu"), "cache_flush_between_steps": flush_buf is not None,
+            "partition_size": ps, "prefix_pages_shared": not args.unshared,
+            "kernel": (("pa_decode_cascade (shared prefix pages read once per group"
+                        + ("; the step's cache write inside the launch)" if fused else ")"))
+                       if groups is not None else
+                       "pa_decode_append (cache write inside the decode launch)" if fused else
+                       "pa_decode" if args.kernel == "auto" else "pa_decode_valu"),
+            "cache_flush_between_steps": flush_buf is not None,
             "parallelism": "none (1 GPU)",
             "shared_prefix_groups": (None if groups is None else
                                      {"groups": int(groups["num_groups"]),
@@ -376,14 +400,12 @@ def run_config(cid, args, headline):
         "bytes": nb,
         "roofline": {
             "bound": "hbm",
-            "kernel": ("decode_valu_kernel" if (wl.dtype != "bf16" or args.kernel != "auto")
-                       else "decode_split_kernel" if ps else "decode_whole_kernel") + f"<{D}>",
+            "kernel": roof_kernel,
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": read_traffic(cid, ps) if (wl.dtype == "bf16" and args.kernel == "auto")
-            else None,
+            "traffic": traffic,
             "algorithmic_bytes_per_launch": launch_bytes,
             "mean_launch_us": round(t_dec * 1e6, 2),
         },

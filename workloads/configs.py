@@ -47,6 +47,10 @@ class DecodeConfig:
     page_size: int = PAGE_SIZE
     # split-KV partition (tokens) the benchmark uses; 0 = single pass
     bench_partition_size: int = 0
+    # the benchmark reads shared prefix pages once per group (pa_decode_cascade),
+    # at this partition size
+    bench_cascade: bool = False
+    cascade_partition_size: int = 0
     # number of sequences that share one prefix (0 = no sharing)
     prefix_group_size: int = 0
     prefix_tokens: int = 0
@@ -75,7 +79,8 @@ CONFIGS = [
     DecodeConfig(3, "prefix_reuse_bf16", 128, 32, 8, 128, "bf16",
                  "batch 128 = 8 groups x 16 sharing a 2048-token prefix, private "
                  "suffixes U[64,512], 32 q / 8 kv heads, D=128, bf16",
-                 bench_partition_size=0, prefix_group_size=16, prefix_tokens=2048),
+                 bench_partition_size=0, prefix_group_size=16, prefix_tokens=2048,
+                 bench_cascade=True, cascade_partition_size=1024),
     DecodeConfig(4, "long_splitkv_bf16", 8, 32, 8, 128, "bf16",
                  "batch 8, lengths U[16384,32768], 32 q / 8 kv heads, D=128, bf16, "
                  "512-token partitions reduced by log-sum-exp",
