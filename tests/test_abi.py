@@ -90,6 +90,84 @@ def test_decode_rejects(fn, name, kw, want):
     assert getattr(pa.load(), fn)(*decode_args(**kw)) == want
 
 
+def append_args(**kw):
+    a = dict(out=None, query=P, key=P, value=P, slot_mapping=P, k_cache=P, v_cache=P,
+             block_tables=P, context_lens=P, num_seqs=4, num_q_heads=32, num_kv_heads=8,
+             head_dim=128, page_size=16, max_pages_per_seq=8, num_pages=64, scale=0.088,
+             partition_size=512, max_num_partitions=4, partial_out=P, partial_max=P,
+             partial_sum=P, dtype=BF16, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+APPEND_CASES = [
+    ("null_key", dict(key=None), INVAL),
+    ("null_value", dict(value=None), INVAL),
+    ("null_slots", dict(slot_mapping=None), INVAL),
+    ("misaligned_key", dict(key=P + 2), INVAL),
+    ("null_query", dict(query=None), INVAL),
+    ("split_without_partials", dict(partial_out=None), INVAL),
+    ("single_pass_without_out", dict(partition_size=0, max_num_partitions=0), INVAL),
+    ("head_dim_96", dict(head_dim=96), UNSUP),
+    ("group_above_16", dict(num_q_heads=32, num_kv_heads=1), UNSUP),
+]
+
+
+@pytest.mark.parametrize("name,kw,want", APPEND_CASES, ids=[c[0] for c in APPEND_CASES])
+def test_decode_append_rejects(name, kw, want):
+    assert pa.load().pa_decode_append(*append_args(**kw)) == want
+
+
+def cascade_args(**kw):
+    a = dict(query=P, key=None, value=None, slot_mapping=None, k_cache=P, v_cache=P,
+             block_tables=P, context_lens=P, num_seqs=4, num_q_heads=32, num_kv_heads=8,
+             head_dim=128, page_size=16, max_pages_per_seq=8, num_pages=64, scale=0.088,
+             partition_size=64, max_num_partitions=2, partial_out=P, partial_max=P,
+             partial_sum=P, num_groups=1, max_group_size=4, max_group_partitions=1,
+             max_suffix_partitions=1, group_start=P, group_seqs=P, group_partitions=P,
+             seq_first_partition=P, dtype=BF16, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+CASCADE_CASES = [
+    ("zero_partition", dict(partition_size=0), INVAL),
+    ("negative_groups", dict(num_groups=-1), INVAL),
+    ("negative_group_size", dict(max_group_size=-1), INVAL),
+    ("negative_group_partitions", dict(max_group_partitions=-1), INVAL),
+    ("negative_suffix_bound", dict(max_suffix_partitions=-1), INVAL),
+    ("group_partitions_above_max", dict(max_group_partitions=3), INVAL),
+    ("null_group_start", dict(group_start=None), INVAL),
+    ("null_group_seqs", dict(group_seqs=None), INVAL),
+    ("null_group_partitions", dict(group_partitions=None), INVAL),
+    ("null_first_partition", dict(seq_first_partition=None), INVAL),
+    ("key_without_value", dict(key=P), INVAL),
+    ("slots_without_key", dict(slot_mapping=P), INVAL),
+    ("f32", dict(dtype=F32), UNSUP),
+    ("head_dim_96", dict(head_dim=96), UNSUP),
+    ("heads_not_divisible", dict(num_q_heads=30), INVAL),
+    ("group_above_16", dict(num_q_heads=32, num_kv_heads=1), UNSUP),
+    ("null_partials", dict(partial_max=None), INVAL),
+    ("misaligned_partials", dict(partial_out=P + 4), INVAL),
+    ("nan_scale", dict(scale=float("nan")), INVAL),
+    ("partition_not_page_multiple", dict(partition_size=40), INVAL),
+]
+
+
+@pytest.mark.parametrize("name,kw,want", CASCADE_CASES, ids=[c[0] for c in CASCADE_CASES])
+def test_cascade_rejects(name, kw, want):
+    assert pa.load().pa_decode_cascade(*cascade_args(**kw)) == want
+
+
+def test_cascade_and_append_empty_batch_is_a_noop():
+    lib = pa.load()
+    assert lib.pa_decode_cascade(*cascade_args(num_seqs=0)) == OK
+    assert lib.pa_decode_cascade(*cascade_args(num_seqs=0, num_groups=0, group_start=None,
+                                               group_seqs=None, group_partitions=None,
+                                               seq_first_partition=None)) == OK
+    assert lib.pa_decode_append(*append_args(num_seqs=0)) == OK
+
+
 def test_decode_empty_batch_is_a_noop():
     lib = pa.load()
     assert lib.pa_decode(*decode_args(num_seqs=0)) == OK
