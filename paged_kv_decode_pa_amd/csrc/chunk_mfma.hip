@@ -26,6 +26,8 @@ namespace pa {
 namespace {
 
 constexpr float kSlack = 8.0f;  // base 2: P may reach 2^8 before a rescale
+constexpr int kChunkRing = 2;   // page tiles per wave in flight or in use (multi-token)
+constexpr int kPrefixRing = 2;  // the same for the shared-prefix units
 
 // One wave's online-softmax state for one block of 16 (token, head) columns.
 template <int D>
@@ -139,16 +141,21 @@ __device__ inline void page_blocks(ColumnAttn<D> (&wa)[NB], const PageTile<D>& t
   for (int nb = 0; nb < NB; ++nb) wa[nb].template accumulate<Masked>(t, s2[nb], lm[nb], raise[nb]);
 }
 
-// Two tiles in ping-pong, as in the decode kernel; ordinal k is page
-// page0 + step * k.  The first loop runs while both pages of a step lie
-// wholly before `visible_end` (every real column of the wave sees all their
-// tokens): far from the diagonal, which is most pages of a long context, the
-// step skips the causal mask and its selects.  One loop per variant keeps a
-// single copy of the page step in each loop body.  The loops stop three
-// ordinals before the end, so the pages they compute are all full (only the
-// sequence's last page can be partial); the last one to three are zeroed
-// past the context first.
-template <int D, int NB>
+// A ring of R tiles per wave; ordinal k is page page0 + step * k.  Pages
+// k .. k+R-1 are computed in turn, each slot refilled with the page R
+// ordinals ahead as soon as it has been used, so R - 1 loads are in flight
+// while a page is computed.  At one wave per SIMD (four column blocks) the
+// wave is alone to hide the memory latency, so the ring is deeper than the
+// decode kernel's two tiles.  The first loop runs while all R pages of a
+// step lie wholly before `visible_end` (every real column of the wave sees
+// all their tokens): far from the diagonal, which is most pages of a long
+// context, the step skips the causal mask and its selects.  One loop per
+// variant keeps a single copy of the page step in each loop body.  The
+// loops stop while every refill still exists (k + 2R <= n), so the pages
+// they compute are all full (only the sequence's last page can be partial);
+// the tail computes the ring's pages, refills what remains, and computes
+// those, each zeroed past the context first.
+template <int D, int NB, int R>
 __device__ inline void run_blocks(ColumnAttn<D> (&wa)[NB], PageStream<D>& ps, int page0, int L,
                                   int visible_end, int lane) {
   const int n = ps.count;
@@ -158,64 +165,73 @@ __device__ inline void run_blocks(ColumnAttn<D> (&wa)[NB], PageStream<D>& ps, in
   // Ordinals below n_clear hold pages wholly before visible_end.
   const int last_clear = visible_end / kPage - 1;  // last page index wholly visible
   const int n_clear = last_clear < page0 ? 0 : (last_clear - page0) / ps.step + 1;
-  PageTile<D> ta, tb;
-  bool ok_a = ps.template issue<false>(ta, 0, lane);
-  bool ok_b = ps.template issue<false>(tb, 1, lane);
+  PageTile<D> t[R];
+  bool ok[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) ok[i] = ps.template issue<false>(t[i], i, lane);
   int k = 0;
-  for (; k + 3 < n && k + 1 < n_clear; k += 2) {
-    if (ok_a) page_blocks<D, NB, false>(wa, ta, base(k));
-    ok_a = ps.template issue<false>(ta, k + 2, lane);
-    if (ok_b) page_blocks<D, NB, false>(wa, tb, base(k + 1));
-    ok_b = ps.template issue<false>(tb, k + 3, lane);
-  }
-  for (; k + 3 < n; k += 2) {
-    if (ok_a) page_blocks<D, NB, true>(wa, ta, base(k));
-    ok_a = ps.template issue<false>(ta, k + 2, lane);
-    if (ok_b) page_blocks<D, NB, true>(wa, tb, base(k + 1));
-    ok_b = ps.template issue<false>(tb, k + 3, lane);
-  }
-  const int rem = n - k;
-  if (ok_a) {
-    zero_past(ta, L - base(k), j);
-    page_blocks<D, NB, true>(wa, ta, base(k));
-  }
-  if (rem >= 2) {
-    const bool ok_c = rem == 3 && ps.template issue<false>(ta, k + 2, lane);
-    if (ok_b) {
-      zero_past(tb, L - base(k + 1), j);
-      page_blocks<D, NB, true>(wa, tb, base(k + 1));
+  for (; k + 2 * R <= n && k + R <= n_clear; k += R) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      if (ok[i]) page_blocks<D, NB, false>(wa, t[i], base(k + i));
+      ok[i] = ps.template issue<false>(t[i], k + i + R, lane);
     }
-    if (ok_c) {
-      zero_past(ta, L - base(k + 2), j);
-      page_blocks<D, NB, true>(wa, ta, base(k + 2));
+  }
+  for (; k + 2 * R <= n; k += R) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      if (ok[i]) page_blocks<D, NB, true>(wa, t[i], base(k + i));
+      ok[i] = ps.template issue<false>(t[i], k + i + R, lane);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    if (k + i < n) {
+      if (ok[i]) {
+        zero_past(t[i], L - base(k + i), j);
+        page_blocks<D, NB, true>(wa, t[i], base(k + i));
+      }
+      ok[i] = k + i + R < n && ps.template issue<false>(t[i], k + i + R, lane);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    if (k + R + i < n && ok[i]) {
+      zero_past(t[i], L - base(k + R + i), j);
+      page_blocks<D, NB, true>(wa, t[i], base(k + R + i));
     }
   }
 }
 
 // Every page of the stream is seen whole by every column (a shared prefix):
-// the mask-free step throughout, and no page is partial.
-template <int D, int NB>
+// the mask-free step throughout, and no page is partial.  Ring as above.
+template <int D, int NB, int R>
 __device__ inline void run_clear(ColumnAttn<D> (&wa)[NB], PageStream<D>& ps, int page0, int lane) {
   const int n = ps.count;
   if (n <= 0) return;
   auto base = [&](int k) { return (page0 + ps.step * k) * kPage; };
-  PageTile<D> ta, tb;
-  bool ok_a = ps.template issue<false>(ta, 0, lane);
-  bool ok_b = ps.template issue<false>(tb, 1, lane);
+  PageTile<D> t[R];
+  bool ok[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) ok[i] = ps.template issue<false>(t[i], i, lane);
   int k = 0;
-  for (; k + 3 < n; k += 2) {
-    if (ok_a) page_blocks<D, NB, false>(wa, ta, base(k));
-    ok_a = ps.template issue<false>(ta, k + 2, lane);
-    if (ok_b) page_blocks<D, NB, false>(wa, tb, base(k + 1));
-    ok_b = ps.template issue<false>(tb, k + 3, lane);
+  for (; k + 2 * R <= n; k += R) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      if (ok[i]) page_blocks<D, NB, false>(wa, t[i], base(k + i));
+      ok[i] = ps.template issue<false>(t[i], k + i + R, lane);
+    }
   }
-  const int rem = n - k;
-  if (ok_a) page_blocks<D, NB, false>(wa, ta, base(k));
-  if (rem >= 2) {
-    const bool ok_c = rem == 3 && ps.template issue<false>(ta, k + 2, lane);
-    if (ok_b) page_blocks<D, NB, false>(wa, tb, base(k + 1));
-    if (ok_c) page_blocks<D, NB, false>(wa, ta, base(k + 2));
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    if (k + i < n) {
+      if (ok[i]) page_blocks<D, NB, false>(wa, t[i], base(k + i));
+      ok[i] = k + i + R < n && ps.template issue<false>(t[i], k + i + R, lane);
+    }
   }
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    if (k + R + i < n && ok[i]) page_blocks<D, NB, false>(wa, t[i], base(k + R + i));
 }
 
 // LDS of the four-wave merge: per wave a reference and a sum per column and
@@ -278,7 +294,7 @@ __global__ __launch_bounds__(kBlock) void chunk_attention_kernel(ChunkParams p) 
   // Tokens below visible_end are seen by every real column of the group (the
   // first column's token sits at the smallest position).
   const int visible_end = L - q_len + c0 / G + 1;
-  run_blocks<D, NB>(wa, ps, w, L, visible_end, lane);
+  run_blocks<D, NB, kChunkRing>(wa, ps, w, L, visible_end, lane);
 
   // Merge the four waves per column (fixed wave order) and store the rows,
   // one block at a time through the same LDS.
@@ -382,7 +398,7 @@ __device__ inline void prefix_unit(const PrefixParams& p, int u, float* smem) {
                            (size_t(seq) * p.num_q_heads + kvh * G + h) * D;
     wa[nb].init(qrow, real, r, j, INT_MAX, p.scale_log2);
   }
-  run_clear<D, NB>(wa, ps, lo + w, lane);
+  run_clear<D, NB, kPrefixRing>(wa, ps, lo + w, lane);
 
   // Merge the four waves per column and write each member's partial for this
   // partition, one block at a time through the same LDS.  The columns'
