@@ -144,9 +144,10 @@ __device__ inline void page_blocks(ColumnAttn<D> (&wa)[NB], const PageTile<D>& t
 // A ring of R tiles per wave; ordinal k is page page0 + step * k.  Pages
 // k .. k+R-1 are computed in turn, each slot refilled with the page R
 // ordinals ahead as soon as it has been used, so R - 1 loads are in flight
-// while a page is computed.  At one wave per SIMD (four column blocks) the
-// wave is alone to hide the memory latency, so the ring is deeper than the
-// decode kernel's two tiles.  The first loop runs while all R pages of a
+// while a page is computed.  (Three or four tiles measured no faster than
+// two at 4 to 64 new tokens, and slower for the shared-prefix units: the
+// page step's own vector and matrix work, not the load latency, sets the
+// pace at one wave per SIMD.)  The first loop runs while all R pages of a
 // step lie wholly before `visible_end` (every real column of the wave sees
 // all their tokens): far from the diagonal, which is most pages of a long
 // context, the step skips the causal mask and its selects.  One loop per
