@@ -132,3 +132,84 @@ def test_suffix_grid_bound(ps):
     for bound in (0, g["max_suffix_partitions"] + 2):
         assert np.array_equal(bits_of(cascade(dev, ps, dict(g, max_suffix_partitions=bound))), tight)
     assert float(np.abs(f64_of(cascade(dev, ps, g)) - oracle_reference(wl)).max()) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_cascade_random(seed):
+    """Seeded random batches: kv heads, group size, head dim, partition size,
+    prefix length, groups scattered through the batch with sequences in none
+    (some empty or one token long), with or without the step's token written
+    in the call.  Against the oracle, and bit for bit against the same call on
+    a pool that already holds the token."""
+    rng = np.random.default_rng(4000 + seed)
+    B = int(rng.integers(2, 40))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    D = int(rng.choice([64, 128]))
+    pp = int(rng.choice([1, 2, 4, 8]))
+    prefix_tokens = 16 * int(rng.integers(pp, 6 * pp + 1))
+    n_groups = int(rng.integers(1, 4))
+    group_of = rng.integers(-1, n_groups, B)
+    lens = np.where(group_of >= 0, prefix_tokens + rng.integers(1, 200, B),
+                    np.where(rng.random(B) < 0.2, rng.integers(0, 2, B), rng.integers(2, 600, B)))
+    append = bool(rng.integers(2))
+    say(f"[cascade random {seed}] B={B} {Hkv * G}/{Hkv}/{D} partition {16 * pp} prefix "
+        f"{prefix_tokens} groups {n_groups} append {append}")
+    wl = make_custom_workload([int(x) for x in lens], num_q_heads=Hkv * G, num_kv_heads=Hkv,
+                              head_dim=D, seed=seed, group_of=group_of.tolist(),
+                              prefix_tokens=prefix_tokens, placement_seed=seed + 5)
+    groups = pa.prefix_groups(wl.block_tables, wl.context_lens, pp)
+    ref_dev = DeviceWorkload(wl)
+    want = cascade(ref_dev, 16 * pp, groups)
+    assert float(np.abs(f64_of(want) - oracle_reference(wl)).max()) <= TOL["bf16"]
+    if append:
+        dev = DeviceWorkload(wl, fill=False)
+        dev.prefill()
+        got = cascade(dev, 16 * pp, groups, append=True)
+        assert np.array_equal(bits_of(dev.k_cache), bits_of(ref_dev.k_cache))
+        assert np.array_equal(bits_of(dev.v_cache), bits_of(ref_dev.v_cache))
+        assert np.array_equal(bits_of(got), bits_of(want))
+
+
+def test_graph_replays_of_the_cascade_step():
+    """The shared-prefix step (with the token write) captured once in a HIP
+    graph and replayed three times, eager work between: every replay equals
+    the eager step bit for bit (the write is idempotent)."""
+    say("[cascade] graph replay")
+    wl = config_workload(3)
+    g0 = pa.prefix_groups(wl.block_tables, wl.context_lens, 64)
+    groups = dev_groups(g0)
+    dev = DeviceWorkload(wl, fill=False)
+    dev.prefill()
+    B, Hq, D = wl.num_seqs, wl.num_q_heads, wl.head_dim
+    n = dev.partition_count(1024)
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=DEV)
+    po = torch.empty((B, Hq, n, D), dtype=torch.float32, device=DEV)
+    pm = torch.empty((B, Hq, n), dtype=torch.float32, device=DEV)
+    psum = torch.empty((B, Hq, n), dtype=torch.float32, device=DEV)
+
+    def step():
+        pa.pa_decode_cascade(dev.query, dev.k_cache, dev.v_cache, dev.block_tables,
+                             dev.context_lens, wl.scale, 1024, po, pm, psum, groups,
+                             key=dev.new_key, value=dev.new_value, slot_mapping=dev.new_slots)
+        pa.pa_decode_reduce(out, po, pm, psum, dev.context_lens, 1024)
+
+    step()
+    torch.cuda.synchronize()
+    want = bits_of(out)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        out.zero_()
+        po.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_of(out), want)
