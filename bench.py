@@ -35,14 +35,21 @@ METRIC = "paged decode attention: achieved KV HBM GB/s (% of peak) + seqs/sec, 1
 PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, vendor peak
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["paged_kv_decode_pa_amd/csrc/decode_mfma.hip",
+                  "paged_kv_decode_pa_amd/csrc/split_plan.hpp",
                   "paged_kv_decode_pa_amd/csrc/wave_attn.hpp",
                   "paged_kv_decode_pa_amd/csrc/page_stream.hpp",
                   "paged_kv_decode_pa_amd/csrc/pa_device.hpp"]
 CHUNK_KERNEL_SOURCES = ["paged_kv_decode_pa_amd/csrc/chunk_mfma.hip",
+                        "paged_kv_decode_pa_amd/csrc/split_plan.hpp",
                         "paged_kv_decode_pa_amd/csrc/wave_attn.hpp",
                         "paged_kv_decode_pa_amd/csrc/page_stream.hpp",
                         "paged_kv_decode_pa_amd/csrc/pa_device.hpp"]
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+# --chunk default: split-KV (pa_chunk_attention_split) at this partition size up
+# to this many new tokens per sequence, the single pass above (measured: the
+# split form is faster at 1 and 2 tokens, even at 4, slower beyond).
+CHUNK_SPLIT_PARTITION = 512
+CHUNK_SPLIT_MAX_Q = 2
 TRANSFER_METRIC = ("KV page hand-off: export every page of the batch to one buffer, import it "
                    "into another pool; GB/s read + written, 1 GPU")
 PAGER_METRIC = ("host page-pool owner: decode steps/s of bookkeeping (one append per "
@@ -100,6 +107,10 @@ def parse_args():
     ap.add_argument("--pager", action="store_true",
                     help="time the host page-pool owner (no GPU): admitting the batch's "
                          "prompts, then decode-step appends and block tables")
+    ap.add_argument("--chunk-partition", type=int, default=None, metavar="PS",
+                    help="with --chunk: pa_chunk_attention_split at this partition size "
+                         "(0 = the single-pass pa_chunk_attention; default: split at 512 "
+                         "tokens up to 2 new tokens per sequence, single pass above)")
     ap.add_argument("--chunk", type=int, default=0, metavar="Q",
                     help="time pa_chunk_attention with Q new tokens per sequence instead of the "
                          "decode step (the cache write of the Q tokens, then the attention)")
@@ -415,10 +426,11 @@ def run_config(cid, args, headline):
     return line
 
 
-def chunk_counts(wl, q):
-    """Algorithmic bytes and flops of one multi-token launch with q new tokens
+def chunk_counts(wl, q, partition_size=0):
+    """Algorithmic bytes and flops of one multi-token call with q new tokens
     per sequence: every cached token's K/V read once (shared prefix pages
-    once), the queries read and the outputs written once; two products of D
+    once), the queries read and the outputs written once, and with split-KV
+    partitions each partial written and read once; two products of D
     multiply-adds per (query token, head, attended position)."""
     esz, B, Hq, Hkv, D = wl.elem_bytes, wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
     L = wl.context_lens.astype(np.int64)
@@ -427,8 +439,13 @@ def chunk_counts(wl, q):
     rows = B * q * Hq * D * esz
     tables = int(((L + 15) // 16).sum()) * 4 + B * 4 + (B + 1) * 4
     attended = int(sum(q * int(l) - q * (q - 1) // 2 for l in L))  # positions L-q .. L-1
+    partials = 0
+    if partition_size:
+        n_parts = (L + partition_size - 1) // partition_size
+        partials = 2 * int(n_parts.sum()) * q * Hq * (D + 2) * 4
     return {"kv_unique": unique_tokens * per_token, "query": rows, "out": rows, "tables": tables,
-            "kernel": unique_tokens * per_token + 2 * rows + tables,
+            "partials": partials,
+            "kernel": unique_tokens * per_token + 2 * rows + tables + partials,
             "cache_write": B * q * (2 * per_token + 8),
             "flops": 4 * D * Hq * attended}
 
@@ -477,6 +494,15 @@ def run_chunk_config(cid, args):
     lens = torch.from_numpy(wl.context_lens).to(dev)
     out = torch.empty_like(query)
     flush_buf = None if args.no_flush else torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+    cps = args.chunk_partition
+    if cps is None:
+        cps = CHUNK_SPLIT_PARTITION if q <= CHUNK_SPLIT_MAX_Q else 0
+    if cps:
+        n_parts = max(1, -(-int(wl.context_lens.max()) // cps))
+        T = B * q
+        po = torch.empty((T, Hq, n_parts, D), dtype=torch.float32, device=dev)
+        pm = torch.empty((T, Hq, n_parts), dtype=torch.float32, device=dev)
+        psum = torch.empty((T, Hq, n_parts), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     def step(ev=None, marks=True):
@@ -485,7 +511,12 @@ def run_chunk_config(cid, args):
         pa.pa_reshape_and_cache(new_k, new_v, k_cache, v_cache, slots_d)
         if ev and marks:
             ev[1].record()
-        pa.pa_chunk_attention(out, query, k_cache, v_cache, tables, lens, query_start, q, wl.scale)
+        if cps:
+            pa.pa_chunk_attention_split(out, query, k_cache, v_cache, tables, lens, query_start, q,
+                                        wl.scale, cps, po, pm, psum)
+        else:
+            pa.pa_chunk_attention(out, query, k_cache, v_cache, tables, lens, query_start, q,
+                                  wl.scale)
         if ev:
             ev[2].record()
 
@@ -514,7 +545,7 @@ def run_chunk_config(cid, args):
     step_ms = [e[0].elapsed_time(e[2]) for e in step_ev]
     cache_ms = [e[0].elapsed_time(e[1]) for e in ev]
     attn_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    nb = chunk_counts(wl, q)
+    nb = chunk_counts(wl, q, cps)
     t_step = float(np.mean(step_ms)) * 1e-3
     t_attn = float(np.mean(attn_ms)) * 1e-3
     gbs = nb["kernel"] / t_attn / 1e9
@@ -527,12 +558,14 @@ def run_chunk_config(cid, args):
              "unit": "TFLOP/s", "frac": round(mfma_frac, 4)})
     kv = read_profile_kv(f"traffic_chunk_attention_cfg{cid}_q{q}.txt", CHUNK_KERNEL_SOURCES)
     traffic = None
-    if kv is not None and not args.unshared:
+    if kv is not None and not args.unshared and int(kv.get("partition_size", 0)) == cps:
         try:
             traffic = float(kv["hbm_bytes_per_launch"])
         except (KeyError, ValueError):
             traffic = None
-    roof.update({"traffic": traffic, "kernel": f"chunk_attention_kernel<{D}>",
+    roof.update({"traffic": traffic,
+                 "kernel": (f"chunk_split_kernel<{D}> + decode_reduce_kernel (one call, "
+                            f"{cps}-token partitions)" if cps else f"chunk_attention_kernel<{D}>"),
                  "algorithmic_bytes_per_launch": nb["kernel"], "flops_per_launch": nb["flops"],
                  "hbm_gbs": round(gbs, 1), "bf16_tflops": round(tflops, 2),
                  "mean_launch_us": round(t_attn * 1e6, 2)})
@@ -545,7 +578,9 @@ def run_chunk_config(cid, args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": WORKLOAD_NAMES[cid] + f"; {q} new tokens per sequence",
-                   "batch": B, "new_tokens_per_seq": q, "q_heads": Hq, "kv_heads": Hkv,
+                   "batch": B, "new_tokens_per_seq": q, "partition_size": cps,
+                   "entry_point": "pa_chunk_attention_split" if cps else "pa_chunk_attention",
+                   "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": D, "page_size": P, "prefix_pages_shared": not args.unshared,
                    "cache_flush_between_steps": flush_buf is not None,
                    "parallelism": "none (1 GPU)"},

@@ -192,6 +192,39 @@ int pa_chunk_attention(void* out, const void* query, const void* k_cache, const 
                        int dtype, void* stream);
 
 /*
+ * pa_chunk_attention_split — pa_chunk_attention as split-KV work units and
+ * their log-sum-exp merge, in one call: for a few new tokens per sequence
+ * (draft verification), where the single-pass units take as long as the
+ * longest sequence.  The same contraction as pa_chunk_attention; the
+ * partitions and their merge are those of pa_decode (split) and
+ * pa_decode_reduce, per new token.
+ *
+ *   partition_size      tokens per partition, a positive multiple of 16.
+ *   max_num_partitions  partition slots per row: ceil(L_b / partition_size)
+ *                       <= max_num_partitions is required of the device data.
+ *   partial_out         [num_query_tokens][num_q_heads][max_num_partitions][head_dim]
+ *                       fp32 (16-byte aligned); partial_max, partial_sum
+ *                       [num_query_tokens][num_q_heads][max_num_partitions]
+ *                       fp32: caller-owned workspace, overwritten.  A token
+ *                       whose position precedes a whole partition gets an
+ *                       empty partial there (o = 0, max = -inf, sum = 0).
+ *   the rest            as in pa_chunk_attention.
+ * Results match pa_chunk_attention to rounding (the partial sums group the
+ * keys by partition) and are deterministic.  Errors as for
+ * pa_chunk_attention, plus PA_ERR_INVALID_ARGUMENT for partition_size <= 0
+ * or not a multiple of 16, max_num_partitions < 1, or a NULL or misaligned
+ * workspace.
+ */
+int pa_chunk_attention_split(void* out, const void* query, const void* k_cache,
+                             const void* v_cache, const int32_t* block_tables,
+                             const int32_t* context_lens, const int32_t* query_start,
+                             int num_seqs, int num_query_tokens, int max_query_len,
+                             int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                             int max_pages_per_seq, int64_t num_pages, float scale,
+                             int partition_size, int max_num_partitions, float* partial_out,
+                             float* partial_max, float* partial_sum, int dtype, void* stream);
+
+/*
  * pa_decode_append — one decode step in one call: write each sequence's new
  * token into the pool, then attend over every cached token.
  *

@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     PaError,
     load,
     pa_chunk_attention,
+    pa_chunk_attention_split,
     pa_decode,
     pa_decode_append,
     pa_decode_cascade,

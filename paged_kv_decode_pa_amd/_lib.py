@@ -47,6 +47,10 @@ _SIGNATURES = {
     "pa_chunk_attention": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                            _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
                            _f32, _i32, _c_void_p],
+    "pa_chunk_attention_split": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                 _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                 _i32, _i64, _f32, _i32, _i32, _c_void_p, _c_void_p, _c_void_p,
+                                 _i32, _c_void_p],
     "pa_decode_reduce": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
                          _i32, _i32, _i32, _c_void_p],
     "pa_export_pages": [_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _i32,
@@ -261,6 +265,34 @@ def pa_chunk_attention(out, query, k_cache, v_cache, block_tables, context_lens,
         _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         _ptr(context_lens), _ptr(query_start), B, T, int(max_query_len), Hq, Hkv, D, PAGE_SIZE,
         block_tables.shape[1], k_cache.shape[0], float(scale), _dtype_code(query),
+        _stream(stream)))
+
+
+def pa_chunk_attention_split(out, query, k_cache, v_cache, block_tables, context_lens,
+                             query_start, max_query_len, scale, partition_size, partial_out,
+                             partial_max, partial_sum, stream=None) -> None:
+    """pa_chunk_attention as split-KV units and their merge, in one call; see
+    include/pa.h.  partial_out [T][Hq][P][D], partial_max / partial_sum
+    [T][Hq][P] fp32 workspace."""
+    T, Hq, D = query.shape
+    B = context_lens.shape[0]
+    Hkv = k_cache.shape[1]
+    if k_cache.shape[2:] != (PAGE_SIZE, D) or v_cache.shape[1:] != (Hkv, D, PAGE_SIZE):
+        raise ValueError("pool shape does not match query")
+    if block_tables.shape[0] != B or tuple(query_start.shape) != (B + 1,):
+        raise ValueError("block_tables / query_start do not match the batch")
+    if out.shape != query.shape or out.dtype != query.dtype:
+        raise ValueError("out must match query")
+    P = partial_max.shape[2]
+    if (partial_out.shape != (T, Hq, P, D) or partial_max.shape != (T, Hq, P)
+            or partial_sum.shape != (T, Hq, P)):
+        raise ValueError("partial buffers have the wrong shape")
+    lib = load()
+    _check("pa_chunk_attention_split", lib.pa_chunk_attention_split(
+        _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        _ptr(context_lens), _ptr(query_start), B, T, int(max_query_len), Hq, Hkv, D, PAGE_SIZE,
+        block_tables.shape[1], k_cache.shape[0], float(scale), int(partition_size), P,
+        _ptr(partial_out), _ptr(partial_max), _ptr(partial_sum), _dtype_code(query),
         _stream(stream)))
 
 

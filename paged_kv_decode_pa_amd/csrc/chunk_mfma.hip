@@ -20,6 +20,7 @@
 // same pages, and the kv-head-fastest unit order puts them on one XCD's L2.
 #include <limits.h>
 
+#include "split_plan.hpp"
 #include "wave_attn.hpp"
 
 namespace pa {
@@ -156,7 +157,7 @@ __device__ inline void page_blocks(ColumnAttn<D> (&wa)[NB], const PageTile<D>& t
 // they compute are all full (only the sequence's last page can be partial);
 // the tail computes the ring's pages, refills what remains, and computes
 // those, each zeroed past the context first.
-template <int D, int NB, int R>
+template <int D, int NB, int R, bool Stream = false>
 __device__ inline void run_blocks(ColumnAttn<D> (&wa)[NB], PageStream<D>& ps, int page0, int L,
                                   int visible_end, int lane) {
   const int n = ps.count;
@@ -169,20 +170,20 @@ __device__ inline void run_blocks(ColumnAttn<D> (&wa)[NB], PageStream<D>& ps, in
   PageTile<D> t[R];
   bool ok[R];
 #pragma unroll
-  for (int i = 0; i < R; ++i) ok[i] = ps.template issue<false>(t[i], i, lane);
+  for (int i = 0; i < R; ++i) ok[i] = ps.template issue<Stream>(t[i], i, lane);
   int k = 0;
   for (; k + 2 * R <= n && k + R <= n_clear; k += R) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       if (ok[i]) page_blocks<D, NB, false>(wa, t[i], base(k + i));
-      ok[i] = ps.template issue<false>(t[i], k + i + R, lane);
+      ok[i] = ps.template issue<Stream>(t[i], k + i + R, lane);
     }
   }
   for (; k + 2 * R <= n; k += R) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       if (ok[i]) page_blocks<D, NB, true>(wa, t[i], base(k + i));
-      ok[i] = ps.template issue<false>(t[i], k + i + R, lane);
+      ok[i] = ps.template issue<Stream>(t[i], k + i + R, lane);
     }
   }
 #pragma unroll
@@ -192,7 +193,7 @@ __device__ inline void run_blocks(ColumnAttn<D> (&wa)[NB], PageStream<D>& ps, in
         zero_past(t[i], L - base(k + i), j);
         page_blocks<D, NB, true>(wa, t[i], base(k + i));
       }
-      ok[i] = k + i + R < n && ps.template issue<false>(t[i], k + i + R, lane);
+      ok[i] = k + i + R < n && ps.template issue<Stream>(t[i], k + i + R, lane);
     }
   }
 #pragma unroll
@@ -336,6 +337,114 @@ __global__ __launch_bounds__(kBlock) void chunk_attention_kernel(ChunkParams p) 
       const int head = kvh * G + cc % G;
       Elem<uint16_t>::store(p.out, (size_t(row) * p.num_q_heads + head) * D + d,
                             wsum > 0.f ? num / wsum : 0.f);
+    }
+  }
+}
+
+// Split-KV form for a few new tokens per sequence (draft verification): the
+// single-pass units above take as long as their longest sequence's four
+// waves, so here one wave per (sequence, partition, kv head, column group)
+// streams the partition's pages and writes each of its (token, head)
+// columns' partial straight from registers, as the split decode does, with
+// the decode's device-side unit plan (full partitions first, no unit past a
+// context) and its load policy (the nontemporal hint for pages that only
+// this unit reads).  A column whose position precedes the whole partition
+// sees none of its keys: its partial is empty (o = 0, m = -inf, l = 0),
+// which the merge weighs by 0.
+template <int D, int NB, int NC>
+__global__ __launch_bounds__(64) void chunk_split_kernel(ChunkParams p) {
+  const int u = blockIdx.x;
+  if (u >= p.num_units) return;
+  const int kvh = u % p.num_kv_heads;
+  const int rest = u / p.num_kv_heads;
+  const int grp = rest % p.groups_per_seq;
+  const int useq = rest / p.groups_per_seq;
+  const int lane = threadIdx.x;
+  const int r = lane & 15, j = lane >> 4;
+  const int G = p.group;
+
+  int seq, part, seq_pages = 0;
+  if constexpr (NC > 0) {
+    if (!split_unit<NC>(p, useq, lane, seq, part, seq_pages)) return;
+  } else {
+    seq = useq % p.num_seqs;  // plain grid: partitions past a context exit below
+    part = useq / p.num_seqs;
+  }
+  seq = __builtin_amdgcn_readfirstlane(seq);
+  part = __builtin_amdgcn_readfirstlane(part);
+
+  // Issued together before any of them returns: the sharing test, the token
+  // offsets, the length and the partition's page ids.
+  SharingTest<NC> sharing;
+  sharing.request(p, lane);
+  const int qa = p.query_start[seq];
+  const int qb = p.query_start[seq + 1];
+  const int L_raw = p.context_lens[seq];
+  const int PP = p.pages_per_partition;
+  const int lo = part * PP;
+  PageStream<D> ps;
+  ps.table = p.block_tables + size_t(seq) * p.max_pages_per_seq;
+  ps.first = lo;
+  ps.step = 1;
+  ps.row_end = min(lo + PP, p.max_pages_per_seq);
+  ps.kpool = static_cast<const char*>(p.k_cache);
+  ps.vpool = static_cast<const char*>(p.v_cache);
+  ps.num_pages = p.num_pages;
+  ps.num_kv_heads = p.num_kv_heads;
+  ps.kvh = kvh;
+  ps.koff = uint32_t(r * D + 8 * j) * 2u;
+  ps.voff = uint32_t(r * kPage + 4 * j) * 2u;
+  ps.start(lane);
+
+  const int q0 = qa;
+  const int q_len = qb - qa;
+  const int cols = q_len * G;
+  const int c0 = grp * NB * 16;
+  if (q_len <= 0 || c0 >= cols || q0 < 0 || q0 + q_len > p.num_query_tokens) return;
+  const int L = min(L_raw, p.max_pages_per_seq * kPage);
+  const int n = (L + kPage - 1) / kPage;
+  if (lo >= n) return;  // partition past the context: the merge does not read it
+  // Pages this group's last column can see (its token is the group's latest).
+  const int last_pos = L - q_len + (min(c0 + NB * 16 - 1, cols - 1) / G);
+  const int hi = max(lo, min(min(lo + PP, n), last_pos >= 0 ? last_pos / kPage + 1 : 0));
+  ps.count = hi - lo;
+
+  ColumnAttn<D> wa[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int c = c0 + 16 * nb + r;
+    const bool real = c < cols;
+    const int i = real ? c / G : 0;
+    const int h = real ? c % G : 0;
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.query) +
+                           (size_t(q0 + i) * p.num_q_heads + kvh * G + h) * D;
+    wa[nb].init(qrow, real, r, j, real ? L - q_len + i : -1, p.scale_log2);
+  }
+  const int visible_end = L - q_len + c0 / G + 1;
+  // One reader per page: a single column group and a sequence whose pages
+  // no other sequence holds.
+  if (p.groups_per_seq == 1 && !sharing.shared(p, seq, lane))
+    run_blocks<D, NB, kChunkRing, true>(wa, ps, lo, L, visible_end, lane);
+  else
+    run_blocks<D, NB, kChunkRing, false>(wa, ps, lo, L, visible_end, lane);
+
+  // Partials of this partition: o = acc / l, m in natural-log units, l.
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int c = c0 + 16 * nb + r;
+    const float l = __shfl(wa[nb].acc[D / 16][0], r);  // row 0 of the denominator block
+    if (c < cols) {
+      const size_t row =
+          (size_t(q0 + c / G) * p.num_q_heads + kvh * G + c % G) * p.num_partitions + part;
+      float* dst = p.partial_out + row * D;
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+        *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * j) = wa[nb].acc[db] * inv;
+      if (j == 0) {
+        p.partial_max[row] = l > 0.f ? wa[nb].m_run * kLn2 : -INFINITY;
+        p.partial_sum[row] = l;
+      }
     }
   }
 }
@@ -512,6 +621,31 @@ hipError_t launch_cascade(const PrefixParams& q, const DecodeParams& p, int head
 }
 
 hipError_t launch_chunk_attention(const ChunkParams& p, int head_dim, hipStream_t stream) {
+  if (p.pages_per_partition > 0) {
+    const dim3 grid(p.num_units);
+#define PA_CHUNK_SPLIT(DD, NBB)                                                          \
+  switch (plan_chunks_for(p.num_seqs)) {                                                 \
+    case 1: chunk_split_kernel<DD, NBB, 1><<<grid, 64, 0, stream>>>(p); break;           \
+    case 4: chunk_split_kernel<DD, NBB, 4><<<grid, 64, 0, stream>>>(p); break;           \
+    case kPlanChunks: chunk_split_kernel<DD, NBB, kPlanChunks><<<grid, 64, 0, stream>>>(p); break; \
+    default: chunk_split_kernel<DD, NBB, 0><<<grid, 64, 0, stream>>>(p); break;          \
+  }
+#define PA_CHUNK_SPLIT_D(DD)                                   \
+  switch (p.blocks_per_wave) {                                 \
+    case 1: PA_CHUNK_SPLIT(DD, 1); break;                      \
+    case 2: PA_CHUNK_SPLIT(DD, 2); break;                      \
+    case 3: PA_CHUNK_SPLIT(DD, 3); break;                      \
+    default: PA_CHUNK_SPLIT(DD, 4); break;                     \
+  }
+    if (head_dim == 128) {
+      PA_CHUNK_SPLIT_D(128)
+    } else {
+      PA_CHUNK_SPLIT_D(64)
+    }
+#undef PA_CHUNK_SPLIT_D
+#undef PA_CHUNK_SPLIT
+    return hipGetLastError();
+  }
   const size_t lds = chunk_lds_bytes(head_dim);
   if (head_dim == 128)
     launch_d<128>(p, lds, stream);

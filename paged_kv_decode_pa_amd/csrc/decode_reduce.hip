@@ -50,16 +50,36 @@ struct RowSet {
   }
 };
 
+// Rows of the multi-token split form: grid row (b * max_query_len + i) *
+// num_q_heads + h is token i of sequence b, head h; its partials and output
+// sit at token row query_start[b] + i, and its partitions are those of the
+// sequence's context.  Decode rows have no token table (query_start NULL).
+struct TokenRows {
+  const int32_t* query_start;  // [num_seqs + 1] or NULL
+  int max_query_len;
+  int num_query_tokens;
+};
+
 template <typename OutT, int D>
 __global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_kernel(
     void* out, const float* __restrict__ part_out, const float* __restrict__ part_max,
     const float* __restrict__ part_sum, const int32_t* __restrict__ context_lens, int num_rows,
-    int num_q_heads, int partition_size, int max_parts) {
+    int num_q_heads, int partition_size, int max_parts, TokenRows tok) {
   constexpr int VD = D / 64;  // output dims per lane
-  const int row = blockIdx.x * kReduceWaves + (threadIdx.x >> 6);  // seq * num_q_heads + head
+  int row = blockIdx.x * kReduceWaves + (threadIdx.x >> 6);  // seq * num_q_heads + head
   if (row >= num_rows) return;
   const int lane = threadIdx.x & 63;
-  const int L = context_lens[row / num_q_heads];
+  int seq = row / num_q_heads;
+  if (tok.query_start) {
+    const int h = row % num_q_heads;
+    const int i = seq % tok.max_query_len;
+    seq /= tok.max_query_len;
+    const int q0 = tok.query_start[seq];
+    const int q_len = tok.query_start[seq + 1] - q0;
+    if (i >= q_len || q0 < 0 || q0 + q_len > tok.num_query_tokens) return;
+    row = (q0 + i) * num_q_heads + h;
+  }
+  const int L = context_lens[seq];
   int n = L > 0 ? (L + partition_size - 1) / partition_size : 0;
   if (n > max_parts) n = max_parts;
   float acc[VD];
@@ -108,16 +128,17 @@ __global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_kernel(
 
 template <typename OutT>
 hipError_t launch_t(void* out, const float* part_out, const float* part_max, const float* part_sum,
-                    const int32_t* context_lens, int num_seqs, int num_q_heads, int head_dim,
-                    int partition_size, int max_parts, hipStream_t stream) {
-  const int rows = num_seqs * num_q_heads;
+                    const int32_t* context_lens, int rows, int num_q_heads, int head_dim,
+                    int partition_size, int max_parts, TokenRows tok, hipStream_t stream) {
   const dim3 grid((rows + kReduceWaves - 1) / kReduceWaves);
   if (head_dim == 128)
     decode_reduce_kernel<OutT, 128><<<grid, 64 * kReduceWaves, 0, stream>>>(
-        out, part_out, part_max, part_sum, context_lens, rows, num_q_heads, partition_size, max_parts);
+        out, part_out, part_max, part_sum, context_lens, rows, num_q_heads, partition_size,
+        max_parts, tok);
   else
     decode_reduce_kernel<OutT, 64><<<grid, 64 * kReduceWaves, 0, stream>>>(
-        out, part_out, part_max, part_sum, context_lens, rows, num_q_heads, partition_size, max_parts);
+        out, part_out, part_max, part_sum, context_lens, rows, num_q_heads, partition_size,
+        max_parts, tok);
   return hipGetLastError();
 }
 
@@ -127,10 +148,23 @@ hipError_t launch_decode_reduce(void* out, const float* part_out, const float* p
                                 const float* part_sum, const int32_t* context_lens, int num_seqs,
                                 int num_q_heads, int head_dim, int partition_size, int max_parts,
                                 bool bf16, hipStream_t stream) {
-  return bf16 ? launch_t<uint16_t>(out, part_out, part_max, part_sum, context_lens, num_seqs,
-                                   num_q_heads, head_dim, partition_size, max_parts, stream)
-              : launch_t<float>(out, part_out, part_max, part_sum, context_lens, num_seqs,
-                                num_q_heads, head_dim, partition_size, max_parts, stream);
+  const TokenRows none{nullptr, 1, 0};
+  const int rows = num_seqs * num_q_heads;
+  return bf16 ? launch_t<uint16_t>(out, part_out, part_max, part_sum, context_lens, rows,
+                                   num_q_heads, head_dim, partition_size, max_parts, none, stream)
+              : launch_t<float>(out, part_out, part_max, part_sum, context_lens, rows,
+                                num_q_heads, head_dim, partition_size, max_parts, none, stream);
+}
+
+hipError_t launch_chunk_reduce(void* out, const float* part_out, const float* part_max,
+                               const float* part_sum, const int32_t* context_lens,
+                               const int32_t* query_start, int num_seqs, int max_query_len,
+                               int num_query_tokens, int num_q_heads, int head_dim,
+                               int partition_size, int max_parts, hipStream_t stream) {
+  const TokenRows tok{query_start, max_query_len, num_query_tokens};
+  const int rows = num_seqs * max_query_len * num_q_heads;
+  return launch_t<uint16_t>(out, part_out, part_max, part_sum, context_lens, rows, num_q_heads,
+                            head_dim, partition_size, max_parts, tok, stream);
 }
 
 }  // namespace pa

@@ -24,6 +24,11 @@ hipError_t launch_decode_reduce(void* out, const float* part_out, const float* p
                                 const float* part_sum, const int32_t* context_lens, int num_seqs,
                                 int num_q_heads, int head_dim, int partition_size, int max_parts,
                                 bool bf16, hipStream_t stream);
+hipError_t launch_chunk_reduce(void* out, const float* part_out, const float* part_max,
+                               const float* part_sum, const int32_t* context_lens,
+                               const int32_t* query_start, int num_seqs, int max_query_len,
+                               int num_query_tokens, int num_q_heads, int head_dim,
+                               int partition_size, int max_parts, hipStream_t stream);
 }  // namespace pa
 
 namespace {
@@ -166,6 +171,81 @@ int page_copy_impl(bool export_dir, void* buffer, int64_t buffer_bytes, void* k_
   return err == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+// Multi-token attention, single pass (partition_size 0) or split-KV with the
+// merge in the same call.
+int chunk_impl(void* out, const void* query, const void* k_cache, const void* v_cache,
+               const int32_t* block_tables, const int32_t* context_lens,
+               const int32_t* query_start, int num_seqs, int num_query_tokens, int max_query_len,
+               int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+               int max_pages_per_seq, int64_t num_pages, float scale, int partition_size,
+               int max_num_partitions, float* partial_out, float* partial_max,
+               float* partial_sum, int dtype, void* stream) {
+  if (num_seqs < 0 || num_query_tokens < 0 || max_query_len < 0 || num_q_heads <= 0 ||
+      num_kv_heads <= 0 || max_pages_per_seq <= 0 || num_pages <= 0)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (int s = check_common(head_dim, page_size, dtype)) return s;
+  if (dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;  // matrix-core kernel only
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARGUMENT;
+  const int group = num_q_heads / num_kv_heads;
+  if (group > PA_MAX_GQA_GROUP) return PA_ERR_UNSUPPORTED;
+  if (!out || !query || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(query) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_ERR_INVALID_ARGUMENT;
+  if (!isfinite(scale)) return PA_ERR_INVALID_ARGUMENT;
+  if (max_query_len > num_query_tokens) return PA_ERR_INVALID_ARGUMENT;
+  const bool split = partition_size > 0;
+  if (split) {
+    if (partition_size % PA_PAGE_SIZE != 0 || max_num_partitions < 1) return PA_ERR_INVALID_ARGUMENT;
+    if (!partial_out || !partial_max || !partial_sum || !aligned16(partial_out))
+      return PA_ERR_INVALID_ARGUMENT;
+  }
+  const int64_t blocks = (int64_t(max_query_len) * group + 15) / 16;
+  const int64_t per_wave = blocks < 4 ? (blocks > 0 ? blocks : 1) : 4;
+  const int64_t groups = (blocks + per_wave - 1) / per_wave;
+  const int64_t units =
+      int64_t(num_seqs) * num_kv_heads * groups * (split ? max_num_partitions : 1);
+  if (units > INT_MAX / 2) return PA_ERR_UNSUPPORTED;
+  if (int64_t(num_query_tokens) * num_q_heads * (split ? max_num_partitions : 1) > INT_MAX ||
+      int64_t(num_seqs) * max_query_len * num_q_heads > INT_MAX)
+    return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0) return PA_OK;
+
+  pa::ChunkParams p;
+  p.out = out;
+  p.query = query;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.query_start = query_start;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = group;
+  p.max_pages_per_seq = max_pages_per_seq;
+  p.num_pages = num_pages;
+  p.scale_log2 = scale * pa::kLog2e;
+  p.num_query_tokens = num_query_tokens;
+  p.blocks_per_wave = int(per_wave);
+  p.groups_per_seq = int(groups);
+  p.num_units = int(units);
+  p.pages_per_partition = split ? partition_size / PA_PAGE_SIZE : 0;
+  p.num_partitions = split ? max_num_partitions : 1;
+  p.partial_out = partial_out;
+  p.partial_max = partial_max;
+  p.partial_sum = partial_sum;
+  p.first_partition = nullptr;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (pa::launch_chunk_attention(p, head_dim, st) != hipSuccess) return PA_ERR_LAUNCH;
+  if (split && pa::launch_chunk_reduce(out, partial_out, partial_max, partial_sum, context_lens,
+                                       query_start, num_seqs, max_query_len, num_query_tokens,
+                                       num_q_heads, head_dim, partition_size, max_num_partitions,
+                                       st) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -294,48 +374,25 @@ int pa_chunk_attention(void* out, const void* query, const void* k_cache, const 
                        int max_query_len, int num_q_heads, int num_kv_heads, int head_dim,
                        int page_size, int max_pages_per_seq, int64_t num_pages, float scale,
                        int dtype, void* stream) {
-  if (num_seqs < 0 || num_query_tokens < 0 || max_query_len < 0 || num_q_heads <= 0 ||
-      num_kv_heads <= 0 || max_pages_per_seq <= 0 || num_pages <= 0)
-    return PA_ERR_INVALID_ARGUMENT;
-  if (int s = check_common(head_dim, page_size, dtype)) return s;
-  if (dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;  // matrix-core kernel only
-  if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARGUMENT;
-  const int group = num_q_heads / num_kv_heads;
-  if (group > PA_MAX_GQA_GROUP) return PA_ERR_UNSUPPORTED;
-  if (!out || !query || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
-    return PA_ERR_INVALID_ARGUMENT;
-  if (!aligned16(query) || !aligned16(k_cache) || !aligned16(v_cache))
-    return PA_ERR_INVALID_ARGUMENT;
-  if (!isfinite(scale)) return PA_ERR_INVALID_ARGUMENT;
-  if (max_query_len > num_query_tokens) return PA_ERR_INVALID_ARGUMENT;
-  const int64_t blocks = (int64_t(max_query_len) * group + 15) / 16;
-  const int64_t per_wave = blocks < 4 ? (blocks > 0 ? blocks : 1) : 4;
-  const int64_t groups = (blocks + per_wave - 1) / per_wave;
-  const int64_t units = int64_t(num_seqs) * num_kv_heads * groups;
-  if (units > INT_MAX / 2) return PA_ERR_UNSUPPORTED;
-  if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0) return PA_OK;
+  return chunk_impl(out, query, k_cache, v_cache, block_tables, context_lens, query_start,
+                    num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads,
+                    head_dim, page_size, max_pages_per_seq, num_pages, scale, 0, 0, nullptr,
+                    nullptr, nullptr, dtype, stream);
+}
 
-  pa::ChunkParams p;
-  p.out = out;
-  p.query = query;
-  p.k_cache = k_cache;
-  p.v_cache = v_cache;
-  p.block_tables = block_tables;
-  p.context_lens = context_lens;
-  p.query_start = query_start;
-  p.num_seqs = num_seqs;
-  p.num_q_heads = num_q_heads;
-  p.num_kv_heads = num_kv_heads;
-  p.group = group;
-  p.max_pages_per_seq = max_pages_per_seq;
-  p.num_pages = num_pages;
-  p.scale_log2 = scale * pa::kLog2e;
-  p.num_query_tokens = num_query_tokens;
-  p.blocks_per_wave = int(per_wave);
-  p.groups_per_seq = int(groups);
-  p.num_units = int(units);
-  const hipError_t err = pa::launch_chunk_attention(p, head_dim, static_cast<hipStream_t>(stream));
-  return err == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+int pa_chunk_attention_split(void* out, const void* query, const void* k_cache,
+                             const void* v_cache, const int32_t* block_tables,
+                             const int32_t* context_lens, const int32_t* query_start,
+                             int num_seqs, int num_query_tokens, int max_query_len,
+                             int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                             int max_pages_per_seq, int64_t num_pages, float scale,
+                             int partition_size, int max_num_partitions, float* partial_out,
+                             float* partial_max, float* partial_sum, int dtype, void* stream) {
+  if (partition_size <= 0) return PA_ERR_INVALID_ARGUMENT;
+  return chunk_impl(out, query, k_cache, v_cache, block_tables, context_lens, query_start,
+                    num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads,
+                    head_dim, page_size, max_pages_per_seq, num_pages, scale, partition_size,
+                    max_num_partitions, partial_out, partial_max, partial_sum, dtype, stream);
 }
 
 int pa_export_pages(void* buffer, int64_t buffer_bytes, const void* k_cache, const void* v_cache,

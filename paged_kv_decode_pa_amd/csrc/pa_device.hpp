@@ -106,7 +106,16 @@ struct ChunkParams {
   int num_query_tokens;
   int blocks_per_wave;  // column blocks a wave carries: min(4, ceil(max_query_len * group / 16))
   int groups_per_seq;   // ceil(ceil(max_query_len * group / 16) / blocks_per_wave)
-  int num_units;        // num_seqs * num_kv_heads * groups_per_seq
+  int num_units;        // num_seqs * num_kv_heads * groups_per_seq (* num_partitions if split)
+  // Split-KV (pages_per_partition > 0): one wave per (sequence, partition, kv
+  // head, column group) writes each of its tokens' partials, rows indexed
+  // like `out`: partial_out[(t * num_q_heads + head) * num_partitions + part][D].
+  int pages_per_partition;
+  int num_partitions;
+  float* partial_out;
+  float* partial_max;
+  float* partial_sum;
+  const int32_t* first_partition;  // always NULL here (the unit plan's field)
 };
 
 // Number of workgroups: one per work unit.

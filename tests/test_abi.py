@@ -211,6 +211,43 @@ def test_chunk_attention_rejects(name, kw, want):
     assert pa.load().pa_chunk_attention(*chunk_args(**kw)) == want
 
 
+def split_chunk_args(**kw):
+    a = dict(out=P, query=P, k_cache=P, v_cache=P, block_tables=P, context_lens=P,
+             query_start=P, num_seqs=4, num_query_tokens=16, max_query_len=4, num_q_heads=32,
+             num_kv_heads=8, head_dim=128, page_size=16, max_pages_per_seq=8, num_pages=64,
+             scale=0.088, partition_size=64, max_num_partitions=2, partial_out=P,
+             partial_max=P, partial_sum=P, dtype=BF16, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+SPLIT_CHUNK_CASES = [
+    ("zero_partition", dict(partition_size=0), INVAL),
+    ("negative_partition", dict(partition_size=-16), INVAL),
+    ("partition_not_page_multiple", dict(partition_size=40), INVAL),
+    ("zero_max_partitions", dict(max_num_partitions=0), INVAL),
+    ("null_partial_out", dict(partial_out=None), INVAL),
+    ("null_partial_max", dict(partial_max=None), INVAL),
+    ("null_partial_sum", dict(partial_sum=None), INVAL),
+    ("misaligned_partials", dict(partial_out=P + 4), INVAL),
+    ("null_query_start", dict(query_start=None), INVAL),
+    ("max_q_above_tokens", dict(max_query_len=17), INVAL),
+    ("f32", dict(dtype=F32), UNSUP),
+    ("head_dim_96", dict(head_dim=96), UNSUP),
+]
+
+
+@pytest.mark.parametrize("name,kw,want", SPLIT_CHUNK_CASES, ids=[c[0] for c in SPLIT_CHUNK_CASES])
+def test_split_chunk_attention_rejects(name, kw, want):
+    assert pa.load().pa_chunk_attention_split(*split_chunk_args(**kw)) == want
+
+
+def test_split_chunk_attention_empty_is_a_noop():
+    lib = pa.load()
+    assert lib.pa_chunk_attention_split(*split_chunk_args(num_seqs=0)) == OK
+    assert lib.pa_chunk_attention_split(*split_chunk_args(num_query_tokens=0, max_query_len=0)) == OK
+
+
 def test_chunk_attention_empty_is_a_noop():
     lib = pa.load()
     assert lib.pa_chunk_attention(*chunk_args(num_seqs=0)) == OK
