@@ -131,6 +131,18 @@ struct pa_pager {
   }
 };
 
+namespace {
+// Length of the common prefix of a[0..n) and b[0..n): whole 16-id blocks
+// by memcmp (vectorised), then the first differing block id by id.
+int common_prefix(const int32_t* a, const int32_t* b, int n) {
+  constexpr int kBlock = 16;
+  int l = 0;
+  while (l + kBlock <= n && std::memcmp(a + l, b + l, kBlock * sizeof(int32_t)) == 0) l += kBlock;
+  while (l < n && a[l] == b[l]) ++l;
+  return l;
+}
+}  // namespace
+
 extern "C" {
 
 pa_pager* pa_pager_create(int64_t num_pages, int page_size, int max_pages_per_seq) {
@@ -340,42 +352,47 @@ int pa_pager_prefix_groups(const int32_t* block_tables, const int32_t* context_l
     const int L = context_lens[b];
     return std::min(L > 0 ? (L - 1) / P : 0, max_pages_per_seq);
   };
-  // Buckets by the page in column 0, in order of first appearance.
-  std::unordered_map<int32_t, size_t> bucket_of;
-  std::vector<std::vector<int64_t>> buckets;
+  // Eligible sequences keyed by the page in column 0.  Sorting the (page,
+  // sequence) pairs makes every bucket a run whose members are in batch
+  // order; the runs are then taken in order of their first member.
+  std::vector<std::pair<int32_t, int32_t>> keyed;
+  keyed.reserve(size_t(num_seqs));
   for (int64_t b = 0; b < num_seqs; ++b) {
     seq_first_partition[b] = 0;
-    if (whole(b) < pages_per_partition) continue;
-    auto it = bucket_of.find(row(b)[0]);
-    if (it == bucket_of.end()) {
-      bucket_of.emplace(row(b)[0], buckets.size());
-      buckets.push_back({b});
-    } else {
-      buckets[it->second].push_back(b);
-    }
+    if (whole(b) >= pages_per_partition) keyed.emplace_back(row(b)[0], int32_t(b));
   }
+  std::sort(keyed.begin(), keyed.end());
+  struct Run {
+    int32_t first_member, begin, end;
+  };
+  std::vector<Run> runs;
+  for (size_t i = 0; i < keyed.size();) {
+    size_t k = i + 1;
+    while (k < keyed.size() && keyed[k].first == keyed[i].first) ++k;
+    if (k - i >= 2) runs.push_back({keyed[i].second, int32_t(i), int32_t(k)});
+    i = k;
+  }
+  std::sort(runs.begin(), runs.end(),
+            [](const Run& a, const Run& b) { return a.first_member < b.first_member; });
   int64_t g = 0, at = 0, max_size = 0, max_parts = 0;
   group_start[0] = 0;
-  for (const auto& members : buckets) {
-    if (members.size() < 2) continue;
-    const int32_t* first = row(members[0]);
-    int lcp = whole(members[0]);
-    for (size_t i = 1; i < members.size(); ++i) {
-      const int32_t* r = row(members[i]);
-      const int lim = std::min(lcp, whole(members[i]));
-      int l = 0;
-      while (l < lim && r[l] == first[l]) ++l;
-      lcp = l;
+  for (const Run& run : runs) {
+    const int32_t* first = row(run.first_member);
+    int lcp = whole(run.first_member);
+    for (int32_t i = run.begin + 1; i < run.end && lcp > 0; ++i) {
+      const int32_t* r = row(keyed[size_t(i)].second);
+      lcp = common_prefix(r, first, std::min(lcp, whole(keyed[size_t(i)].second)));
     }
     const int parts = lcp / pages_per_partition;
     if (parts < 1) continue;
-    for (int64_t b : members) {
-      group_seqs[at++] = int32_t(b);
+    for (int32_t i = run.begin; i < run.end; ++i) {
+      const int32_t b = keyed[size_t(i)].second;
+      group_seqs[at++] = b;
       seq_first_partition[b] = parts;
     }
     group_partitions[g] = parts;
     group_start[++g] = int32_t(at);
-    max_size = std::max<int64_t>(max_size, int64_t(members.size()));
+    max_size = std::max<int64_t>(max_size, run.end - run.begin);
     max_parts = std::max<int64_t>(max_parts, parts);
   }
   int64_t max_suffix = 0;
