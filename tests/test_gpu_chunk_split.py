@@ -80,3 +80,43 @@ def test_tokens_that_precede_a_partition():
     dev = DeviceWorkload(wl)
     got = run_split(dev, query, qs, 512)
     assert max_err(got, chunk_reference(wl, query, qs)) <= TOL["bf16"]
+
+
+def test_split_beyond_planned_batch_size():
+    """More than 1024 sequences: the split kernel's plain grid (no unit plan,
+    cached loads throughout)."""
+    say("[chunk split] 1100-sequence batch")
+    rng = np.random.default_rng(15)
+    lens = rng.integers(1, 80, size=1100)
+    q_lens = [int(rng.integers(0, min(int(L), 3) + 1)) for L in lens]
+    wl = make_custom_workload(lens.tolist(), num_q_heads=8, num_kv_heads=1, head_dim=128, seed=16)
+    query, qs = make_chunk_queries(wl, q_lens, seed=17)
+    ref = chunk_reference(wl, query, qs)
+    dev = DeviceWorkload(wl)
+    for ps in (16, 32):
+        assert max_err(run_split(dev, query, qs, ps), ref) <= TOL["bf16"], ps
+
+
+@pytest.mark.parametrize("B", [48, 200])
+def test_split_with_scattered_prefix_sharing(B):
+    """Sequences sharing prefix pages anywhere in the batch: those stream their
+    pages through the caches, the others with the nontemporal hint; shared and
+    private copies of the same values give identical bits, and match the
+    oracle."""
+    say(f"[chunk split] scattered prefix sharing, batch {B}")
+    rng = np.random.default_rng(B + 1)
+    group_of = np.where(rng.random(B) < 0.4, rng.integers(0, 5, B), -1)
+    prefix = 64
+    lens = np.where(group_of >= 0, rng.integers(prefix + 4, 400, B), rng.integers(4, 400, B))
+    q_lens = rng.integers(1, 4, B).tolist()
+    kw = dict(num_q_heads=8, num_kv_heads=2, head_dim=128, seed=B, prefix_tokens=prefix,
+              group_of=group_of.tolist())
+    shared = make_custom_workload(lens.tolist(), **kw)
+    private = make_custom_workload(lens.tolist(), share_prefix=False, **kw)
+    query, qs = make_chunk_queries(shared, q_lens, seed=B)
+    ref = chunk_reference(shared, query, qs)
+    ds, dp = DeviceWorkload(shared), DeviceWorkload(private)
+    for ps in (64, 256):
+        a = run_split(ds, query, qs, ps)
+        assert np.array_equal(bits_of(a), bits_of(run_split(dp, query, qs, ps))), ps
+        assert max_err(a, ref) <= TOL["bf16"], ps
