@@ -87,8 +87,9 @@ struct FirstPages {
 // every wave reads all context lengths and derives the same list.  Per kv
 // head, the full partitions come first in partition-major order (partition 0
 // of every sequence, then partition 1, ...) and each sequence's partly filled
-// last partition comes after all of them, so the longest units are dispatched
-// first and no wave is spent on a partition past a context's end.  Returns
+// last partition comes after all of them, largest first, so the longest
+// units are dispatched first and no wave is spent on a partition past a
+// context's end.  Returns
 // false for an index past the last unit.  NC * 64 >= batch.
 template <int NC, class Params>
 __device__ bool split_unit(const Params& p, int useq, int lane, int& seq, int& part,
@@ -140,16 +141,25 @@ __device__ bool split_unit(const Params& p, int useq, int lane, int& seq, int& p
       k -= n;
     }
   } else {
+    // Partly filled partitions, largest first (ties in batch order).  Blocks
+    // are placed on CUs by index (block b on XCD b % 8, then the XCD's CUs
+    // in turn), so after the full partitions the first of these land on the
+    // CUs that got one full partition fewer: the largest go there.
     int k = useq - full_total;
+    int psize[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const uint64_t m = __ballot(hasp[c] != 0);
-      const int n = __popcll(m);
-      if (seq < 0 && k < n && k >= 0) {
-        seq = 64 * c + kth_set_lane(m, k, lane);
-        part = __builtin_amdgcn_readlane(nfull[c] + first[c], seq - 64 * c);
+    for (int c = 0; c < NC; ++c) psize[c] = hasp[c] ? pages[c] - (pages[c] / PP) * PP : 0;
+    for (int sz = PP - 1; sz >= 1 && seq < 0; --sz) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const uint64_t m = __ballot(hasp[c] != 0 && psize[c] == sz);
+        const int n = __popcll(m);
+        if (seq < 0 && k < n && k >= 0) {
+          seq = 64 * c + kth_set_lane(m, k, lane);
+          part = __builtin_amdgcn_readlane(nfull[c] + first[c], seq - 64 * c);
+        }
+        k -= n;
       }
-      k -= n;
     }
   }
   seq = __builtin_amdgcn_readfirstlane(seq);
