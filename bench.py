@@ -46,10 +46,10 @@ CHUNK_KERNEL_SOURCES = ["paged_kv_decode_pa_amd/csrc/chunk_mfma.hip",
                         "paged_kv_decode_pa_amd/csrc/pa_device.hpp"]
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 # --chunk default: split-KV (pa_chunk_attention_split) at this partition size up
-# to this many new tokens per sequence, the single pass above (measured: the
-# split form is faster at 1 and 2 tokens, even at 4, slower beyond).
-CHUNK_SPLIT_PARTITION = 512
-CHUNK_SPLIT_MAX_Q = 2
+# to this many new tokens per sequence, the single pass above (measured on the
+# Llama-3-8B batch: the split form is faster up to 8 tokens, slower at 16).
+CHUNK_SPLIT_PARTITION = 768
+CHUNK_SPLIT_MAX_Q = 8
 TRANSFER_METRIC = ("KV page hand-off: export every page of the batch to one buffer, import it "
                    "into another pool; GB/s read + written, 1 GPU")
 PAGER_METRIC = ("host page-pool owner: decode steps/s of bookkeeping (one append per "
@@ -109,8 +109,8 @@ def parse_args():
                          "prompts, then decode-step appends and block tables")
     ap.add_argument("--chunk-partition", type=int, default=None, metavar="PS",
                     help="with --chunk: pa_chunk_attention_split at this partition size "
-                         "(0 = the single-pass pa_chunk_attention; default: split at 512 "
-                         "tokens up to 2 new tokens per sequence, single pass above)")
+                         "(0 = the single-pass pa_chunk_attention; default: split at 768 "
+                         "tokens up to 8 new tokens per sequence, single pass above)")
     ap.add_argument("--chunk", type=int, default=0, metavar="Q",
                     help="time pa_chunk_attention with Q new tokens per sequence instead of the "
                          "decode step (the cache write of the Q tokens, then the attention)")

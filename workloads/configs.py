@@ -80,7 +80,7 @@ CONFIGS = [
                  "batch 128 = 8 groups x 16 sharing a 2048-token prefix, private "
                  "suffixes U[64,512], 32 q / 8 kv heads, D=128, bf16",
                  bench_partition_size=0, prefix_group_size=16, prefix_tokens=2048,
-                 bench_cascade=True, cascade_partition_size=1024),
+                 bench_cascade=True, cascade_partition_size=2048),
     DecodeConfig(4, "long_splitkv_bf16", 8, 32, 8, 128, "bf16",
                  "batch 8, lengths U[16384,32768], 32 q / 8 kv heads, D=128, bf16, "
                  "512-token partitions reduced by log-sum-exp",
