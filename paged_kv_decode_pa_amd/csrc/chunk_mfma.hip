@@ -18,6 +18,15 @@
 // online-softmax states of each block merge through LDS in a fixed order.
 // Pages are read with cached loads: a long chunk's block groups reread the
 // same pages, and the kv-head-fastest unit order puts them on one XCD's L2.
+//
+// The same column machinery serves three more kernels here:
+//   chunk_split_kernel  the split-KV form of the above (one wave per
+//                       sequence, partition, kv head and column group, with
+//                       the decode's unit plan), merged by the reduce kernel;
+//   prefix_unit         a shared prefix's partition read once per group, the
+//                       members' query heads as the columns;
+//   cascade_kernel      prefix units and the decode's four-wave units of each
+//                       sequence's own partitions in one grid.
 #include <limits.h>
 
 #include "split_plan.hpp"
