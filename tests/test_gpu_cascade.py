@@ -11,7 +11,7 @@ import oracle
 import paged_kv_decode_pa_amd as pa
 from tests.gpu_helpers import (DEV, TOL, DeviceWorkload, bits_of, config_workload, f64_of,
                                oracle_reference, say, tdtype)
-from workloads import make_custom_workload
+from workloads import config_by_id, make_custom_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -39,7 +39,7 @@ def cascade(dev, ps, groups, append=False):
     return out
 
 
-@pytest.mark.parametrize("ps", [256, 512])
+@pytest.mark.parametrize("ps", sorted({256, 512, 1024, config_by_id(3).cascade_partition_size}))
 def test_prefix_reuse_workload(ps):
     say(f"[cascade] prefix-reuse batch, partition {ps}")
     wl = config_workload(3)

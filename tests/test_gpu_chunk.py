@@ -85,6 +85,31 @@ def test_spec_decode_batch_at_config_2_shape():
     assert max_err(got, ref) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("q", [16, 64])
+def test_bench_shape_on_sampled_sequences(q):
+    """q new tokens for each of config 2's 64 sequences, the single-pass launch
+    that the multi-token bench times at q > 8.  The GPU runs the whole batch;
+    the oracle checks eight sequences (the longest, the shortest and six
+    seeded picks), every row of each."""
+    say(f"[chunk] config 2 shape, {q} new tokens per sequence, sampled oracle")
+    wl = config_workload(2)
+    query, qs = make_chunk_queries(wl, [q] * wl.num_seqs, seed=q)
+    got = run_chunk(config_device(2), query, qs).float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    lens = np.asarray(wl.context_lens)
+    rng = np.random.default_rng(q)
+    pick = sorted({int(lens.argmax()), int(lens.argmin()),
+                   *rng.choice(wl.num_seqs, 6, replace=False).tolist()})
+    k, v = fill_pools(oracle, wl)
+    for b in pick:
+        lo, hi = int(qs[b]), int(qs[b + 1])
+        ref = oracle.chunk_attention(query[lo:hi], k, v, wl.block_tables[b:b + 1],
+                                     wl.context_lens[b:b + 1], np.array([0, hi - lo]),
+                                     wl.scale, wl.page_size, wl.dtype)
+        err = float(np.abs(got[lo:hi] - ref).max())
+        assert err <= TOL["bf16"], (b, err)
+
+
 def test_later_tokens_never_reach_earlier_rows():
     say("[chunk] causality on the GPU")
     wl = make_custom_workload([200], num_q_heads=8, num_kv_heads=2, head_dim=128, seed=5)

@@ -48,7 +48,7 @@ def test_split_matches_oracle(lens, q_lens, Hq, Hkv, D, ps):
     assert np.array_equal(bits_of(run_split(dev, query, qs, ps)), bits_of(got))  # deterministic
 
 
-@pytest.mark.parametrize("cid,ps", [(2, 512), (5, 256), (4, 512)])
+@pytest.mark.parametrize("cid,ps", [(2, 512), (2, 768), (5, 256), (4, 512)])
 def test_one_token_per_sequence_is_split_decode(cid, ps):
     say(f"[chunk split] q_len = 1 equals split decode + reduce, config {cid}")
     dev = config_device(cid)
@@ -58,14 +58,16 @@ def test_one_token_per_sequence_is_split_decode(cid, ps):
     assert np.array_equal(bits_of(got), bits_of(dev.decode(ps)))
 
 
-@pytest.mark.parametrize("q", [2, 4, 8])
-def test_draft_verification_at_config_2_shape(q):
-    """q new tokens for each of config 2's 64 sequences, 512-token partitions."""
-    say(f"[chunk split] config 2 shape, {q} new tokens per sequence")
+@pytest.mark.parametrize("q,ps", [(2, 512), (4, 512), (8, 512), (1, 768), (2, 768), (4, 768),
+                                  (8, 768)])
+def test_draft_verification_at_config_2_shape(q, ps):
+    """q new tokens for each of config 2's 64 sequences; 768-token partitions
+    are the split form's default at this shape (q <= 8)."""
+    say(f"[chunk split] config 2 shape, {q} new tokens per sequence, partition {ps}")
     wl = config_workload(2)
     query, qs = make_chunk_queries(wl, [q] * wl.num_seqs, seed=q)
-    dev = DeviceWorkload(wl)
-    got = run_split(dev, query, qs, 512)
+    dev = config_device(2)
+    got = run_split(dev, query, qs, ps)
     assert max_err(got, chunk_reference(wl, query, qs)) <= TOL["bf16"]
 
 
