@@ -40,9 +40,13 @@ constexpr int kChunkRing = 2;   // page tiles per wave in flight or in use (mult
 constexpr int kPrefixRing = 2;  // the same for the shared-prefix units
 
 // One wave's online-softmax state for one block of 16 (token, head) columns.
-template <int D>
+// The query operands live in registers, or (QL) in LDS shared by the
+// workgroup's waves, read again for every page: that frees D / 8 registers
+// per block, which lets four-block waves run two to a SIMD.
+template <int D, bool QL = false>
 struct ColumnAttn {
-  bf16x8 qop[D / 32];    // B operand: column r = (token, head) pair r of the block
+  bf16x8 qop[QL ? 1 : D / 32];  // B operand: column r = (token, head) pair r of the block
+  const bf16x8* qlds;    // QL: this lane's operand of k-step kb at qlds[64 * kb]
   s16x4 ones;            // A operand of the denominator block
   f32x4 acc[D / 16 + 1]; // O^T blocks (lane: dims 16db+4j.., column r), then the denominator
   float m_run;           // base-2 reference score of column r (equal in its 4 lane groups)
@@ -60,11 +64,40 @@ struct ColumnAttn {
       if (real) v = *reinterpret_cast<const u32x4*>(qrow + 32 * kb + 8 * j);
       qop[kb] = __builtin_bit_cast(bf16x8, v);
     }
+    init_state(r);
+  }
+
+  // QL: `slot` is this lane's LDS operand slot of the block; a writer wave
+  // fills it from the query row (zero for a padding column).  The caller
+  // synchronises the workgroup before the first page.
+  __device__ void init_lds(bf16x8* slot, bool writer, const uint16_t* qrow, bool real, int r,
+                           int j_, int pos_, float sl2) {
+    j = j_;
+    pos = pos_;
+    scale_log2 = sl2;
+    qlds = slot;
+    if (writer) {
+#pragma unroll
+      for (int kb = 0; kb < D / 32; ++kb) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (real) v = *reinterpret_cast<const u32x4*>(qrow + 32 * kb + 8 * j);
+        slot[64 * kb] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+    init_state(r);
+  }
+
+  __device__ void init_state(int r) {
     ones = s16x4{0, 0, 0, 0};
     if (r == 0) ones = s16x4{0x3F80, 0x3F80, 0x3F80, 0x3F80};
     m_run = -INFINITY;
 #pragma unroll
     for (int db = 0; db <= D / 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  __device__ bf16x8 q(int kb) const {
+    if constexpr (QL) return qlds[64 * kb];
+    else return qop[kb];
   }
 
   // Scores of the page starting at token `base`, base 2.  Masked: with the
@@ -75,7 +108,7 @@ struct ColumnAttn {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < D / 32; ++kb)
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[kb], qop[kb], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[kb], q(kb), s, 0, 0, 0);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if constexpr (Masked)
@@ -135,8 +168,8 @@ __device__ inline void zero_past(PageTile<D>& t, int valid, int j) {
 // the reads of its result, the compiler was seen to let a taken branch reach
 // the reads fewer wait states after the instruction than the result needs
 // (wrong, run-to-run varying scores).
-template <int D, int NB, bool Masked>
-__device__ inline void page_blocks(ColumnAttn<D> (&wa)[NB], const PageTile<D>& t, int base) {
+template <int D, int NB, bool Masked, bool QL>
+__device__ inline void page_blocks(ColumnAttn<D, QL> (&wa)[NB], const PageTile<D>& t, int base) {
   float s2[NB][4];
   float lm[NB];
   bool raise[NB];
@@ -166,8 +199,8 @@ __device__ inline void page_blocks(ColumnAttn<D> (&wa)[NB], const PageTile<D>& t
 // they compute are all full (only the sequence's last page can be partial);
 // the tail computes the ring's pages, refills what remains, and computes
 // those, each zeroed past the context first.
-template <int D, int NB, int R, bool Stream = false>
-__device__ inline void run_blocks(ColumnAttn<D> (&wa)[NB], PageStream<D>& ps, int page0, int L,
+template <int D, int NB, int R, bool Stream = false, bool QL = false>
+__device__ inline void run_blocks(ColumnAttn<D, QL> (&wa)[NB], PageStream<D>& ps, int page0, int L,
                                   int visible_end, int lane) {
   const int n = ps.count;
   if (n <= 0) return;
@@ -184,14 +217,14 @@ __device__ inline void run_blocks(ColumnAttn<D> (&wa)[NB], PageStream<D>& ps, in
   for (; k + 2 * R <= n && k + R <= n_clear; k += R) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      if (ok[i]) page_blocks<D, NB, false>(wa, t[i], base(k + i));
+      if (ok[i]) page_blocks<D, NB, false, QL>(wa, t[i], base(k + i));
       ok[i] = ps.template issue<Stream>(t[i], k + i + R, lane);
     }
   }
   for (; k + 2 * R <= n; k += R) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      if (ok[i]) page_blocks<D, NB, true>(wa, t[i], base(k + i));
+      if (ok[i]) page_blocks<D, NB, true, QL>(wa, t[i], base(k + i));
       ok[i] = ps.template issue<Stream>(t[i], k + i + R, lane);
     }
   }
@@ -200,7 +233,7 @@ __device__ inline void run_blocks(ColumnAttn<D> (&wa)[NB], PageStream<D>& ps, in
     if (k + i < n) {
       if (ok[i]) {
         zero_past(t[i], L - base(k + i), j);
-        page_blocks<D, NB, true>(wa, t[i], base(k + i));
+        page_blocks<D, NB, true, QL>(wa, t[i], base(k + i));
       }
       ok[i] = k + i + R < n && ps.template issue<Stream>(t[i], k + i + R, lane);
     }
@@ -209,7 +242,7 @@ __device__ inline void run_blocks(ColumnAttn<D> (&wa)[NB], PageStream<D>& ps, in
   for (int i = 0; i < R; ++i) {
     if (k + R + i < n && ok[i]) {
       zero_past(t[i], L - base(k + R + i), j);
-      page_blocks<D, NB, true>(wa, t[i], base(k + R + i));
+      page_blocks<D, NB, true, QL>(wa, t[i], base(k + R + i));
     }
   }
 }
@@ -229,20 +262,20 @@ __device__ inline void run_clear(ColumnAttn<D> (&wa)[NB], PageStream<D>& ps, int
   for (; k + 2 * R <= n; k += R) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      if (ok[i]) page_blocks<D, NB, false>(wa, t[i], base(k + i));
+      if (ok[i]) page_blocks<D, NB, false, false>(wa, t[i], base(k + i));
       ok[i] = ps.template issue<false>(t[i], k + i + R, lane);
     }
   }
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     if (k + i < n) {
-      if (ok[i]) page_blocks<D, NB, false>(wa, t[i], base(k + i));
+      if (ok[i]) page_blocks<D, NB, false, false>(wa, t[i], base(k + i));
       ok[i] = k + i + R < n && ps.template issue<false>(t[i], k + i + R, lane);
     }
   }
 #pragma unroll
   for (int i = 0; i < R; ++i)
-    if (k + R + i < n && ok[i]) page_blocks<D, NB, false>(wa, t[i], base(k + R + i));
+    if (k + R + i < n && ok[i]) page_blocks<D, NB, false, false>(wa, t[i], base(k + R + i));
 }
 
 // LDS of the four-wave merge: per wave a reference and a sum per column and
@@ -251,8 +284,16 @@ __host__ __device__ inline size_t chunk_lds_bytes(int head_dim) {
   return sizeof(float) * (2 * kWaves * 16 + size_t(kWaves) * 16 * (head_dim + kAccPad));
 }
 
+// Waves of three or four column blocks keep the query operands in LDS, after
+// the merge's area: 16 bytes per lane and k-step of each block.
+constexpr bool chunk_query_in_lds(int nb) { return nb >= 3; }
+__host__ __device__ inline size_t chunk_query_lds_bytes(int head_dim, int nb) {
+  return chunk_query_in_lds(nb) ? size_t(nb) * (head_dim / 32) * 64 * 16 : 0;
+}
+
 template <int D, int NB>
-__global__ __launch_bounds__(kBlock) void chunk_attention_kernel(ChunkParams p) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(NB >= 3 ? 2 : 1)))
+void chunk_attention_kernel(ChunkParams p) {
   extern __shared__ float smem[];
   const int u = blockIdx.x;
   if (u >= p.num_units) return;
@@ -290,7 +331,9 @@ __global__ __launch_bounds__(kBlock) void chunk_attention_kernel(ChunkParams p) 
   ps.start(lane);
   ps.count = w < n_pages ? (n_pages - w + kWaves - 1) / kWaves : 0;
 
-  ColumnAttn<D> wa[NB];
+  constexpr bool QL = chunk_query_in_lds(NB);
+  bf16x8* qslots = reinterpret_cast<bf16x8*>(smem + chunk_lds_bytes(D) / sizeof(float));
+  ColumnAttn<D, QL> wa[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int c = c0 + 16 * nb + r;
@@ -300,12 +343,18 @@ __global__ __launch_bounds__(kBlock) void chunk_attention_kernel(ChunkParams p) 
     const uint16_t* qrow = static_cast<const uint16_t*>(p.query) +
                            (size_t(q0 + i) * p.num_q_heads + kvh * G + h) * D;
     // position of the column's token (< 0 only if q_len exceeds the context)
-    wa[nb].init(qrow, real, r, j, real ? L - q_len + i : -1, p.scale_log2);
+    const int pos = real ? L - q_len + i : -1;
+    if constexpr (QL)  // wave nb writes block nb's operands
+      wa[nb].init_lds(qslots + (nb * (D / 32)) * 64 + lane, w == nb, qrow, real, r, j, pos,
+                      p.scale_log2);
+    else
+      wa[nb].init(qrow, real, r, j, pos, p.scale_log2);
   }
+  if constexpr (QL) __syncthreads();
   // Tokens below visible_end are seen by every real column of the group (the
   // first column's token sits at the smallest position).
   const int visible_end = L - q_len + c0 / G + 1;
-  run_blocks<D, NB, kChunkRing>(wa, ps, w, L, visible_end, lane);
+  run_blocks<D, NB, kChunkRing, false, QL>(wa, ps, w, L, visible_end, lane);
 
   // Merge the four waves per column (fixed wave order) and store the rows,
   // one block at a time through the same LDS.
@@ -600,14 +649,18 @@ __global__ __launch_bounds__(kBlock) void cascade_kernel(PrefixParams q, DecodeP
 }
 
 template <int D>
-void launch_d(const ChunkParams& p, size_t lds, hipStream_t stream) {
+void launch_d(const ChunkParams& p, hipStream_t stream) {
   const dim3 grid(p.num_units);
+  const size_t lds = chunk_lds_bytes(D);
+#define PA_CHUNK(NBB) \
+  chunk_attention_kernel<D, NBB><<<grid, kBlock, lds + chunk_query_lds_bytes(D, NBB), stream>>>(p)
   switch (p.blocks_per_wave) {
-    case 1: chunk_attention_kernel<D, 1><<<grid, kBlock, lds, stream>>>(p); break;
-    case 2: chunk_attention_kernel<D, 2><<<grid, kBlock, lds, stream>>>(p); break;
-    case 3: chunk_attention_kernel<D, 3><<<grid, kBlock, lds, stream>>>(p); break;
-    default: chunk_attention_kernel<D, 4><<<grid, kBlock, lds, stream>>>(p); break;
+    case 1: PA_CHUNK(1); break;
+    case 2: PA_CHUNK(2); break;
+    case 3: PA_CHUNK(3); break;
+    default: PA_CHUNK(4); break;
   }
+#undef PA_CHUNK
 }
 
 }  // namespace
@@ -655,11 +708,10 @@ hipError_t launch_chunk_attention(const ChunkParams& p, int head_dim, hipStream_
 #undef PA_CHUNK_SPLIT
     return hipGetLastError();
   }
-  const size_t lds = chunk_lds_bytes(head_dim);
   if (head_dim == 128)
-    launch_d<128>(p, lds, stream);
+    launch_d<128>(p, stream);
   else
-    launch_d<64>(p, lds, stream);
+    launch_d<64>(p, stream);
   return hipGetLastError();
 }
 
