@@ -16,6 +16,8 @@
 // read.  Unit = (sequence, kv head, group of NB blocks), four waves; wave w
 // takes pages w, w+4, ... up to the group's last position, and the four
 // online-softmax states of each block merge through LDS in a fixed order.
+// With three or four blocks the query operands sit in LDS (each wave writes
+// one block's), which keeps a wave within 256 registers, two per SIMD.
 // Pages are read with cached loads: a long chunk's block groups reread the
 // same pages, and the kv-head-fastest unit order puts them on one XCD's L2.
 //
