@@ -37,6 +37,9 @@
 namespace pa {
 namespace {
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 constexpr float kSlack = 8.0f;  // base 2: P may reach 2^8 before a rescale
 constexpr int kChunkRing = 2;   // page tiles per wave in flight or in use (multi-token)
 constexpr int kPrefixRing = 2;  // the same for the shared-prefix units
@@ -138,15 +141,20 @@ struct ColumnAttn {
 #pragma unroll
       for (int db = 0; db <= D / 16; ++db) acc[db] *= alpha;
     }
-    s16x4 pb;
+    // P to bf16 (round to nearest even) two at a time; a masked score gives 0.
+    float pf[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const short p = static_cast<short>(f32_to_bf16(__builtin_amdgcn_exp2f(s2[e] - m_run)));
+      const float p = __builtin_amdgcn_exp2f(s2[e] - m_run);
       if constexpr (Masked)
-        pb[e] = s2[e] == -INFINITY ? short(0) : p;
+        pf[e] = s2[e] == -INFINITY ? 0.f : p;
       else
-        pb[e] = p;
+        pf[e] = p;
     }
+    const bf16x2 lo2 = __builtin_convertvector((f32x2){pf[0], pf[1]}, bf16x2);
+    const bf16x2 hi2 = __builtin_convertvector((f32x2){pf[2], pf[3]}, bf16x2);
+    const s16x4 pb = __builtin_bit_cast(
+        s16x4, (u32x2){__builtin_bit_cast(uint32_t, lo2), __builtin_bit_cast(uint32_t, hi2)});
 #pragma unroll
     for (int db = 0; db < D / 16; ++db)
       acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[db], pb, acc[db], 0, 0, 0);
