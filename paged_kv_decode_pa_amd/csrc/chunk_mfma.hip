@@ -301,17 +301,67 @@ __host__ __device__ inline size_t chunk_query_lds_bytes(int head_dim, int nb) {
   return chunk_query_in_lds(nb) ? size_t(nb) * (head_dim / 32) * 64 * 16 : 0;
 }
 
+// The sequence of rank `rank` when the batch is ordered by context length
+// (clamped to the table), longest first, ties in batch order; a batch above
+// kPlanMaxSeqs keeps its order.  Units are dispatched in grid order, so the
+// long sequences' units start first and the short ones fill in behind them,
+// instead of a long sequence's units starting late and setting the end.
+// The rank's length is found by a binary search on the count of lengths at
+// or above a threshold (wave ballots), then the tie by its batch order.
+__device__ inline int longest_first(const ChunkParams& p, int rank, int lane) {
+  if (p.num_seqs > kPlanMaxSeqs) return rank;
+  const int nc = (p.num_seqs + 63) >> 6;
+  const int cap = min(p.max_pages_per_seq, (1 << 30) / kPage - 1) * kPage;
+  int len[kPlanChunks];
+#pragma unroll
+  for (int c = 0; c < kPlanChunks; ++c) {
+    const int b = 64 * c + lane;
+    len[c] = -1;  // past the batch
+    if (c < nc && b < p.num_seqs) len[c] = min(max(p.context_lens[b], 0), cap);
+  }
+  int top = 0;
+#pragma unroll
+  for (int c = 0; c < kPlanChunks; ++c) top = max(top, len[c]);
+#pragma unroll
+  for (int x = 1; x < 64; x <<= 1) top = max(top, __shfl_xor(top, x));
+  auto count_ge = [&](int t) {
+    int n = 0;
+#pragma unroll
+    for (int c = 0; c < kPlanChunks; ++c)
+      if (c < nc) n += __popcll(__ballot(len[c] >= t));
+    return n;
+  };
+  int lo = 0, hi = top + 1;  // count_ge(lo) > rank >= count_ge(hi)
+  while (hi - lo > 1) {
+    const int mid = lo + ((hi - lo) >> 1);
+    if (count_ge(mid) > rank) lo = mid; else hi = mid;
+  }
+  int k = rank - count_ge(lo + 1);  // rank among the sequences of length lo
+  int seq = -1;
+#pragma unroll
+  for (int c = 0; c < kPlanChunks; ++c) {
+    if (c < nc) {
+      const uint64_t m = __ballot(len[c] == lo);
+      const int n = __popcll(m);
+      if (seq < 0 && k >= 0 && k < n) seq = 64 * c + kth_set_lane(m, k, lane);
+      k -= n;
+    }
+  }
+  seq = __builtin_amdgcn_readfirstlane(seq);
+  return seq >= 0 ? seq : rank;
+}
+
 template <int D, int NB>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(NB >= 3 ? 2 : 1)))
 void chunk_attention_kernel(ChunkParams p) {
   extern __shared__ float smem[];
   const int u = blockIdx.x;
   if (u >= p.num_units) return;
+  const int lane = threadIdx.x & 63;
   const int kvh = u % p.num_kv_heads;
   const int rest = u / p.num_kv_heads;
   const int grp = rest % p.groups_per_seq;
-  const int seq = rest / p.groups_per_seq;
-  const int lane = threadIdx.x & 63;
+  const int seq = longest_first(p, rest / p.groups_per_seq, lane);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, j = lane >> 4;
   const int G = p.group;

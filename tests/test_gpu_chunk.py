@@ -85,6 +85,25 @@ def test_spec_decode_batch_at_config_2_shape():
     assert max_err(got, ref) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("B", [130, 1100])
+def test_many_sequences_with_equal_lengths(B):
+    """Units run longest sequence first: batches past one 64-sequence ballot
+    chunk (130) and past the ordered range (1100, batch order), with many
+    equal lengths and some new tokens preceding others' contexts; every row
+    against the oracle, and a second call gives the same bits."""
+    say(f"[chunk] {B} sequences, lengths from a few values")
+    rng = np.random.default_rng(B)
+    lens = rng.choice([3, 16, 17, 40, 97], size=B).tolist()
+    wl = make_custom_workload(lens, num_q_heads=8, num_kv_heads=2, head_dim=64, seed=B)
+    q_lens = [min(n, int(rng.integers(1, 6))) for n in lens]
+    query, qs = make_chunk_queries(wl, q_lens, seed=B + 1)
+    ref = chunk_reference(wl, query, qs)
+    dev = DeviceWorkload(wl)
+    got = run_chunk(dev, query, qs)
+    assert max_err(got, ref) <= TOL["bf16"]
+    assert np.array_equal(bits_of(run_chunk(dev, query, qs)), bits_of(got))
+
+
 @pytest.mark.parametrize("q", [16, 64])
 def test_bench_shape_on_sampled_sequences(q):
     """q new tokens for each of config 2's 64 sequences, the single-pass launch
