@@ -122,7 +122,11 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
  *   context_lens   int32 [num_seqs]; L_b counts every cached token of
  *                  sequence b, including one appended this step.  0 yields a
  *                  zero output.  Lengths above 16 * max_pages_per_seq are
- *                  clamped to it.
+ *                  clamped to it; with split-KV, each partition past the
+ *                  clamped context but below min(ceil(L_b / partition_size),
+ *                  max_num_partitions) gets an empty partial (out 0, max
+ *                  -inf, sum 0), so pa_decode_reduce merges the clamped
+ *                  context.
  *   scale          multiplies q . k before the softmax (normally 1/sqrt(D)).
  *   partition_size 0: single pass, `out` is written directly and the partial
  *                  buffers may be NULL.  Otherwise a positive multiple of 16:
@@ -137,7 +141,9 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
  *                  m need not be the exact maximum; any reference that keeps
  *                  the exponentials finite gives the same merged result.
  *   max_num_partitions  partition dimension of the partial buffers (>= 1 when
- *                  splitting).  Partitions at or beyond it are not computed.
+ *                  splitting).  Partitions at or beyond it are not computed
+ *                  and their rows are never written; the merge then covers
+ *                  the first max_num_partitions * partition_size tokens.
  *   partial_out    float32 [num_seqs][num_q_heads][max_num_partitions][head_dim]
  *   partial_max,
  *   partial_sum    float32 [num_seqs][num_q_heads][max_num_partitions]
@@ -279,7 +285,8 @@ int pa_decode_append(void* out, const void* query, const void* key, const void* 
  *               from its first.  A smaller value than the
  *               true maximum leaves partitions uncomputed (unspecified
  *               results); 0 means max_num_partitions (always enough, at the
- *               cost of workgroups that find nothing to do).
+ *               cost of workgroups that find nothing to do).  Units whose
+ *               partition would reach max_num_partitions are skipped.
  *               pa_pager_prefix_groups returns it.
  *   group_start [num_groups + 1], group_seqs, group_partitions [num_groups],
  *   seq_first_partition [num_seqs]: int32, device.  seq_first_partition[b]

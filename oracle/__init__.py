@@ -15,6 +15,7 @@ unpinned".
 from .paged_attention import (  # noqa: F401
     attention,
     bf16_bits_to_float64,
+    bf16_ulp_distance,
     cache_write,
     causal_attention,
     chunk_attention,
@@ -25,5 +26,6 @@ from .paged_attention import (  # noqa: F401
     gather_sequence,
     import_pages,
     partition_attention,
+    round_to_bf16_bits,
     to_float64,
 )

@@ -36,6 +36,8 @@ exactly (a bf16 value is the top 16 bits of an IEEE binary32).
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 
@@ -43,6 +45,52 @@ def bf16_bits_to_float64(bits: np.ndarray) -> np.ndarray:
     """Widen bf16 bit patterns (uint16) to float64, exactly."""
     wide = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     return wide.view(np.float32).astype(np.float64)
+
+
+def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to bf16 (round to nearest, ties to even) in one
+    step, returning the uint16 bit patterns.
+
+    The pages fix no output rounding; the reading taken is that a bf16 output
+    is the exact result rounded once to nearest-even.  bf16 keeps 8
+    significant bits over binary32's exponent range: normal values have the
+    quantum 2^(e - 7) for 2^e <= |x| < 2^(e + 1), e >= -126; below 2^-126 the
+    quantum stays 2^-133 (subnormals).  Magnitudes that round past the largest
+    finite value (2 - 2^-7) * 2^127 become infinity; NaN becomes 0x7FC0.
+    """
+    a = np.asarray(x, dtype=np.float64)
+    flat = a.reshape(-1)
+    out = np.zeros(flat.shape, dtype=np.uint16)
+    for i, v in enumerate(flat.tolist()):
+        if v != v:
+            out[i] = 0x7FC0
+            continue
+        sign = 0x8000 if math.copysign(1.0, v) < 0 else 0
+        m = abs(v)
+        if m == 0.0:
+            out[i] = sign
+            continue
+        if m != math.inf:
+            e = max(math.frexp(m)[1] - 1, -126)    # 2^e <= m < 2^(e+1), or subnormal
+            quantum = math.ldexp(1.0, e - 7)
+            m = round(m / quantum) * quantum       # Python round(): ties to even
+        if m >= math.ldexp(1.0, 128):
+            out[i] = sign | 0x7F80
+            continue
+        # m is now a bf16 value: its binary32 pattern ends in 16 zero bits.
+        bits32 = int(np.array([m], dtype=np.float32).view(np.uint32)[0])
+        out[i] = sign | (bits32 >> 16)
+    return out.reshape(a.shape)
+
+
+def bf16_ulp_distance(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    """Number of bf16 values between two finite bf16 patterns, counted along
+    the number line (+0 and -0 are the same point)."""
+    def ordered(bits):
+        b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+        mag = b & 0x7FFF
+        return np.where(b & 0x8000, -mag, mag)
+    return np.abs(ordered(a_bits) - ordered(b_bits))
 
 
 def to_float64(values: np.ndarray, dtype: str) -> np.ndarray:

@@ -60,7 +60,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   int n = (L + kPage - 1) / kPage;
   if (n > p.max_pages_per_seq) n = p.max_pages_per_seq;
   const int hi = min(lo + p.pages_per_partition, n);
-  if (lo >= hi) return;  // partition past the context: nothing to write
+  if (lo >= hi) {
+    // A partition past the context writes nothing, except one that the merge
+    // counts (past a length clamped to the table's width): an empty partial.
+    if constexpr (NC == 0)
+      if (part < merged_partitions(p, L)) empty_partials<D>(p, seq, kvh, part, part + 1, lane, 64);
+    return;
+  }
   if constexpr (NC == 0) {  // the plain grid learns the length only now
     writes = appends && hi == n;
     if (writes) nt.request(p, seq, kvh, lane);
@@ -84,6 +90,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
       p.partial_sum[row] = l;
     }
   }
+  // The plan has no units past a length clamped to the block table's width;
+  // the unit of the last partition with tokens gives the partitions after it
+  // that the merge counts empty partials.
+  if constexpr (NC > 0)
+    if (hi == n) empty_partials<D>(p, seq, kvh, part + 1, merged_partitions(p, L), lane, 64);
 }
 
 // ---------------------------------------------------------------- single pass

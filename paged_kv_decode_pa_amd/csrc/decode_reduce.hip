@@ -9,6 +9,8 @@
 // ping-pong, and the first set is requested together with the scores and
 // sums: a row of up to 16 partitions costs one memory round trip, 48
 // partitions three.
+#include <limits.h>
+
 #include "pa_device.hpp"
 
 namespace pa {
@@ -54,10 +56,13 @@ struct RowSet {
 // num_q_heads + h is token i of sequence b, head h; its partials and output
 // sit at token row query_start[b] + i, and its partitions are those of the
 // sequence's context.  Decode rows have no token table (query_start NULL).
+// The multi-token kernels clamp a context to the block table's width
+// (max_context tokens) and compute partitions of the clamped context only.
 struct TokenRows {
   const int32_t* query_start;  // [num_seqs + 1] or NULL
   int max_query_len;
   int num_query_tokens;
+  int max_context;             // INT_MAX for decode rows
 };
 
 template <typename OutT, int D>
@@ -79,8 +84,8 @@ __global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_kernel(
     if (i >= q_len || q0 < 0 || q0 + q_len > tok.num_query_tokens) return;
     row = (q0 + i) * num_q_heads + h;
   }
-  const int L = context_lens[seq];
-  int n = L > 0 ? (L + partition_size - 1) / partition_size : 0;
+  const int L = min(context_lens[seq], tok.max_context);
+  int n = L > 0 ? int((int64_t(L) + partition_size - 1) / partition_size) : 0;
   if (n > max_parts) n = max_parts;
   float acc[VD];
 #pragma unroll
@@ -148,7 +153,7 @@ hipError_t launch_decode_reduce(void* out, const float* part_out, const float* p
                                 const float* part_sum, const int32_t* context_lens, int num_seqs,
                                 int num_q_heads, int head_dim, int partition_size, int max_parts,
                                 bool bf16, hipStream_t stream) {
-  const TokenRows none{nullptr, 1, 0};
+  const TokenRows none{nullptr, 1, 0, INT_MAX};
   const int rows = num_seqs * num_q_heads;
   return bf16 ? launch_t<uint16_t>(out, part_out, part_max, part_sum, context_lens, rows,
                                    num_q_heads, head_dim, partition_size, max_parts, none, stream)
@@ -160,8 +165,10 @@ hipError_t launch_chunk_reduce(void* out, const float* part_out, const float* pa
                                const float* part_sum, const int32_t* context_lens,
                                const int32_t* query_start, int num_seqs, int max_query_len,
                                int num_query_tokens, int num_q_heads, int head_dim,
-                               int partition_size, int max_parts, hipStream_t stream) {
-  const TokenRows tok{query_start, max_query_len, num_query_tokens};
+                               int partition_size, int max_parts, int max_pages_per_seq,
+                               hipStream_t stream) {
+  const TokenRows tok{query_start, max_query_len, num_query_tokens,
+                      max_pages_per_seq > INT_MAX / kPage ? INT_MAX : max_pages_per_seq * kPage};
   const int rows = num_seqs * max_query_len * num_q_heads;
   return launch_t<uint16_t>(out, part_out, part_max, part_sum, context_lens, rows, num_q_heads,
                             head_dim, partition_size, max_parts, tok, stream);

@@ -61,7 +61,10 @@ __global__ __launch_bounds__(kBlock) void decode_valu_kernel(DecodeParams p) {
   const int L = p.context_lens[seq];
   int lo, hi;
   if (!unit_pages(p, seq, part, L, lo, hi)) {
-    if (p.pages_per_partition == 0) store_zeros<T, D>(p, seq, kvh);
+    if (p.pages_per_partition == 0)
+      store_zeros<T, D>(p, seq, kvh);
+    else if (part < merged_partitions(p, L))  // past a length clamped to the table
+      empty_partials<D>(p, seq, kvh, part, part + 1, threadIdx.x, kBlock);
     return;
   }
   const int G = p.group;

@@ -28,7 +28,8 @@ hipError_t launch_chunk_reduce(void* out, const float* part_out, const float* pa
                                const float* part_sum, const int32_t* context_lens,
                                const int32_t* query_start, int num_seqs, int max_query_len,
                                int num_query_tokens, int num_q_heads, int head_dim,
-                               int partition_size, int max_parts, hipStream_t stream);
+                               int partition_size, int max_parts, int max_pages_per_seq,
+                               hipStream_t stream);
 }  // namespace pa
 
 namespace {
@@ -241,7 +242,7 @@ int chunk_impl(void* out, const void* query, const void* k_cache, const void* v_
   if (split && pa::launch_chunk_reduce(out, partial_out, partial_max, partial_sum, context_lens,
                                        query_start, num_seqs, max_query_len, num_query_tokens,
                                        num_q_heads, head_dim, partition_size, max_num_partitions,
-                                       st) != hipSuccess)
+                                       max_pages_per_seq, st) != hipSuccess)
     return PA_ERR_LAUNCH;
   return PA_OK;
 }

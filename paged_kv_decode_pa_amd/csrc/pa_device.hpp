@@ -127,25 +127,30 @@ __host__ __device__ inline int decode_grid(int num_units) { return num_units; }
 // kv heads: every XCD gets the same share of every sequence, and all the
 // sequences that share a prefix page read it through one XCD's L2.  With
 // first_partition the partition index counts from the sequence's first.
-__device__ inline bool unit_of(const DecodeParams& p, int u, int& seq, int& kvh, int& part) {
+// A unit whose partition index reaches num_partitions (a sequence's first
+// partition plus a grid bound can exceed it) has no partial row: false.
+__host__ __device__ inline bool unit_of(const DecodeParams& p, int u, int& seq, int& kvh,
+                                        int& part) {
   if (u >= p.num_units) return false;
   kvh = u % p.num_kv_heads;
   const int rest = u / p.num_kv_heads;
   part = rest % p.grid_partitions;
   seq = rest / p.grid_partitions;
-  if (p.first_partition)  // partitions below it are computed elsewhere
-    part += min(max(p.first_partition[seq], 0), p.num_partitions);
-  return true;
+  if (p.first_partition) {  // partitions below it are computed elsewhere
+    const int f = p.first_partition[seq];
+    part += f < 0 ? 0 : f > p.num_partitions ? p.num_partitions : f;
+  }
+  return part < p.num_partitions;
 }
 
 // Page range [lo, hi) of a unit; false when the unit has no tokens.
-__device__ inline bool unit_pages(const DecodeParams& p, int seq, int part, int L, int& lo,
-                                  int& hi) {
+__host__ __device__ inline bool unit_pages(const DecodeParams& p, int seq, int part, int L,
+                                           int& lo, int& hi) {
   int n = (L + kPage - 1) / kPage;
   if (n > p.max_pages_per_seq) n = p.max_pages_per_seq;
   if (p.pages_per_partition > 0) {
     lo = part * p.pages_per_partition;
-    hi = min(lo + p.pages_per_partition, n);
+    hi = lo + p.pages_per_partition < n ? lo + p.pages_per_partition : n;
   } else {
     lo = 0;
     hi = n;
@@ -224,6 +229,37 @@ __device__ inline void merge_and_store(const DecodeParams& p, const MergeLds& s,
         p.partial_max[row] = M * kLn2;  // natural-log units of scale * q.k
         p.partial_sum[row] = wsum;
       }
+    }
+  }
+}
+
+// Split-KV partitions that the merge counts for a context of L tokens:
+// ceil(L / partition size), at most num_partitions.  It counts from the raw
+// length, while the kernels clamp a length to the block table's width, so
+// partitions past the clamped context get empty partials (empty_partials).
+__host__ __device__ inline int merged_partitions(const DecodeParams& p, int L) {
+  if (L <= 0 || p.pages_per_partition <= 0) return 0;
+  const int64_t ps = int64_t(p.pages_per_partition) * kPage;
+  const int64_t n = (int64_t(L) + ps - 1) / ps;
+  return n < p.num_partitions ? int(n) : p.num_partitions;
+}
+
+// Empty partials (o = 0, m = -inf, l = 0; the merge weighs them by 0) for
+// partitions [from, to) of one (sequence, kv head): thread tid of nthreads.
+template <int D>
+__device__ inline void empty_partials(const DecodeParams& p, int seq, int kvh, int from, int to,
+                                      int tid, int nthreads) {
+  const int G = p.group;
+  const int n = to > from ? (to - from) * G * D : 0;
+  for (int idx = tid; idx < n; idx += nthreads) {
+    const int d = idx % D;
+    const int h = (idx / D) % G;
+    const int part = from + idx / (D * G);
+    const size_t row = (size_t(seq) * p.num_q_heads + kvh * G + h) * p.num_partitions + part;
+    p.partial_out[row * D + d] = 0.f;
+    if (d == 0) {
+      p.partial_max[row] = -INFINITY;
+      p.partial_sum[row] = 0.f;
     }
   }
 }

@@ -251,8 +251,11 @@ __device__ inline void whole_unit(const DecodeParams& p, int seq, int kvh, int p
 
   int lo, hi;
   if (!unit_pages(p, seq, part, L, lo, hi)) {
-    if (PP == 0) store_zeros<uint16_t, D>(p, seq, kvh);
-    return;  // a partition past the context writes nothing
+    if (PP == 0)
+      store_zeros<uint16_t, D>(p, seq, kvh);
+    else if (part < merged_partitions(p, L))  // past a length clamped to the table
+      empty_partials<D>(p, seq, kvh, part, part + 1, threadIdx.x, kBlock);
+    return;  // any other partition past the context writes nothing
   }
   const int n = min((L + kPage - 1) / kPage, p.max_pages_per_seq);
   const bool writes = appends && hi == n && (hi - 1 - lo) % kWaves == w && nt.valid(p);

@@ -127,3 +127,23 @@ def max_err(out, ref):
     got = f64_of(out)
     assert np.isfinite(got).all(), "non-finite output"
     return float(np.abs(got - ref).max())
+
+
+def parity_report(out, ref):
+    """Max-abs error, relative error max|err| / max|ref|, and (bf16) the
+    largest distance in bf16 ulps from the oracle's value rounded once to
+    nearest-even."""
+    got = f64_of(out)
+    assert np.isfinite(got).all(), "non-finite output"
+    err = float(np.abs(got - ref).max())
+    scale = float(np.abs(ref).max())
+    rep = {"max_abs": err, "rel": err / scale if scale > 0 else err, "max_ulp": None}
+    if out.dtype == torch.bfloat16:
+        rep["max_ulp"] = int(oracle.bf16_ulp_distance(bits_of(out),
+                                                      oracle.round_to_bf16_bits(ref)).max())
+    return rep
+
+
+def report_line(rep):
+    ulp = "" if rep["max_ulp"] is None else f", max {rep['max_ulp']} bf16 ulp from RNE(oracle)"
+    return f"max abs err {rep['max_abs']:.3e}, rel {rep['rel']:.3e}{ulp}"

@@ -587,8 +587,51 @@ def check_page_handoff_preserves_attention(orc):
     assert np.array_equal(a, c)
 
 
+def check_round_to_bf16(orc):
+    """Round-to-nearest-even onto bf16, from float64 in one step."""
+    cases = [
+        (1.0, 0x3F80), (-2.0, 0xC000), (0.0, 0x0000), (-0.0, 0x8000),
+        (1.0 + 2.0 ** -8, 0x3F80),                 # tie between 0x3F80 and 0x3F81: even
+        (1.0 + 3 * 2.0 ** -8, 0x3F82),             # tie between 0x3F81 and 0x3F82: even
+        (1.0 + 2.0 ** -8 + 2.0 ** -40, 0x3F81),    # just past the tie
+        (1.0 + 2.0 ** -8 - 2.0 ** -40, 0x3F80),    # just short of it
+        (3.140625, 0x4049), (1.0 / 3.0, 0x3EAB), (-1.0 / 3.0, 0xBEAB),
+        (2.0 ** -133, 0x0001),                     # smallest subnormal
+        (2.0 ** -134, 0x0000),                     # tie with zero: even
+        (3 * 2.0 ** -134, 0x0002),                 # tie between 0x0001 and 0x0002
+        (2.0 ** -126 - 2.0 ** -140, 0x0080),       # rounds up to the smallest normal
+        ((2 - 2.0 ** -7) * 2.0 ** 127, 0x7F7F),    # largest finite
+        ((2 - 2.0 ** -8) * 2.0 ** 127, 0x7F80),    # tie with the next step: overflow
+        (1e300, 0x7F80), (-math.inf, 0xFF80),
+    ]
+    got = orc.round_to_bf16_bits(np.array([c[0] for c in cases]))
+    for (x, want), g in zip(cases, got.tolist()):
+        assert g == want, (x, hex(g), hex(want))
+    assert orc.round_to_bf16_bits(np.array([math.nan]))[0] == 0x7FC0
+    # Every finite bf16 value maps to itself.
+    bits = np.arange(0, 1 << 16, 7, dtype=np.uint32).astype(np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]
+    assert np.array_equal(orc.round_to_bf16_bits(orc.bf16_bits_to_float64(bits)), bits)
+    # Library routine: values exactly representable in binary32 round as
+    # torch's float32 -> bfloat16 cast does (one rounding either way).
+    import torch
+    rng = np.random.default_rng(11)
+    x32 = np.concatenate([rng.standard_normal(4000), rng.uniform(-1e-38, 1e-38, 500),
+                          rng.standard_normal(500) * 1e30]).astype(np.float32)
+    want = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(orc.round_to_bf16_bits(x32.astype(np.float64)), want)
+
+
+def check_bf16_ulp_distance(orc):
+    a = np.array([0x3F80, 0x3F80, 0x0000, 0x8000, 0x0001, 0xBF80, 0x7F7F], dtype=np.uint16)
+    b = np.array([0x3F81, 0x3F80, 0x8000, 0x0001, 0x8001, 0xBF82, 0x0000], dtype=np.uint16)
+    assert orc.bf16_ulp_distance(a, b).tolist() == [1, 0, 0, 1, 2, 2, 0x7F7F]
+
+
 ALL_CHECKS = [
     check_bf16_widening,
+    check_round_to_bf16,
+    check_bf16_ulp_distance,
     check_cache_write_layout,
     check_gather_roundtrip,
     check_single_token_returns_v,

@@ -10,7 +10,7 @@ import torch
 import oracle
 import paged_kv_decode_pa_amd as pa
 from tests.gpu_helpers import (DEV, TOL, DeviceWorkload, bits_of, config_workload, f64_of,
-                               oracle_reference, say, tdtype)
+                               oracle_reference, parity_report, report_line, say, tdtype)
 from workloads import config_by_id, make_custom_workload
 
 pytestmark = pytest.mark.gpu
@@ -57,17 +57,24 @@ def test_prefix_reuse_workload(ps):
     assert np.array_equal(bits_of(cascade(dev, ps, groups)), bits_of(got))  # deterministic
 
 
-def test_step_token_written_in_the_same_call():
-    say("[cascade] with the step's token")
+@pytest.mark.parametrize("ps", sorted({512, config_by_id(3).cascade_partition_size}))
+def test_step_token_written_in_the_same_call(ps):
+    """At the benchmarked 2048-token partitions too: pool and output bit for
+    bit against the cascade on a pool that already holds the token, and the
+    output against the oracle."""
+    say(f"[cascade] with the step's token, partition {ps}")
     wl = config_workload(3)
-    groups = pa.prefix_groups(wl.block_tables, wl.context_lens, 32)
+    groups = pa.prefix_groups(wl.block_tables, wl.context_lens, ps // 16)
     ref_dev = DeviceWorkload(wl)
     dev = DeviceWorkload(wl, fill=False)
     dev.prefill()
-    got = cascade(dev, 512, groups, append=True)
+    got = cascade(dev, ps, groups, append=True)
     assert np.array_equal(bits_of(dev.k_cache), bits_of(ref_dev.k_cache))
     assert np.array_equal(bits_of(dev.v_cache), bits_of(ref_dev.v_cache))
-    assert np.array_equal(bits_of(got), bits_of(cascade(ref_dev, 512, groups)))
+    assert np.array_equal(bits_of(got), bits_of(cascade(ref_dev, ps, groups)))
+    rep = parity_report(got, oracle_reference(wl))
+    say("    " + report_line(rep))
+    assert rep["max_abs"] <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (16, 2, 64), (8, 8, 128)])

@@ -12,7 +12,8 @@ import pytest
 import torch
 
 from tests.gpu_helpers import (TOL, DeviceWorkload, bits_of, config_device, config_reference,
-                               config_workload, f64_of, max_err, oracle_reference, say)
+                               config_workload, f64_of, max_err, oracle_reference, parity_report,
+                               report_line, say)
 from workloads import config_by_id, make_custom_workload, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -38,9 +39,9 @@ def test_config_matches_oracle(cid, ps, kernel):
     ref = config_reference(cid)
     dev = config_device(cid)
     out = dev.decode(ps, kernel)
-    err = max_err(out, ref)
-    say(f"    max abs err {err:.3e}")
-    assert err <= TOL[wl.dtype]
+    rep = parity_report(out, ref)
+    say("    " + report_line(rep))
+    assert rep["max_abs"] <= TOL[wl.dtype]
 
 
 @pytest.mark.parametrize("cid", [2, 5])

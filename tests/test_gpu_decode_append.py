@@ -8,8 +8,9 @@ import pytest
 import torch
 
 import paged_kv_decode_pa_amd as pa
-from tests.gpu_helpers import DEV, DeviceWorkload, bits_of, config_workload, say, tdtype
-from workloads import make_custom_workload
+from tests.gpu_helpers import (DEV, TOL, DeviceWorkload, bits_of, config_reference,
+                               config_workload, parity_report, report_line, say, tdtype)
+from workloads import config_by_id, make_custom_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -40,9 +41,15 @@ def fused_step(dev, partition_size, slots=None):
     return out
 
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
-@pytest.mark.parametrize("ps", [0, 256])
+FUSED_CASES = [(cid, ps) for cid in (1, 2, 3, 4, 5)
+               for ps in sorted({0, 256, config_by_id(cid).bench_partition_size})]
+
+
+@pytest.mark.parametrize("cid,ps", FUSED_CASES, ids=[f"cfg{c}-ps{p}" for c, p in FUSED_CASES])
 def test_fused_step_equals_write_then_decode(cid, ps):
+    """At each workload's benchmarked partition too (768, 512 and 256 tokens
+    for configs 2, 4 and 5): the whole pool and the output bit for bit
+    against the two calls, and the output against the oracle."""
     say(f"[decode_append] config {cid}, partition {ps}")
     wl = config_workload(cid)
     ref = DeviceWorkload(wl)                    # prefill + pa_reshape_and_cache
@@ -53,6 +60,9 @@ def test_fused_step_equals_write_then_decode(cid, ps):
     assert np.array_equal(raw(dev.k_cache), raw(ref.k_cache))
     assert np.array_equal(raw(dev.v_cache), raw(ref.v_cache))
     assert np.array_equal(raw(got), raw(want))
+    rep = parity_report(got, config_reference(cid))
+    say("    " + report_line(rep))
+    assert rep["max_abs"] <= TOL[wl.dtype]
 
 
 @pytest.mark.parametrize("ps", [0, 64])

@@ -167,7 +167,52 @@ def _import_wraps_negative(k_cache, v_cache, buffer, page_ids):
     return kc, vc
 
 
+def _round_variant(mode):
+    """Plausible mistakes in the rounding onto bf16."""
+    import math
+
+    def round_to_bf16_bits(x):
+        a = np.asarray(x, dtype=np.float64).reshape(-1)
+        out = np.zeros(a.shape, dtype=np.uint16)
+        for i, v in enumerate(a.tolist()):
+            if v != v:
+                out[i] = 0x7FC0
+                continue
+            if mode == "via_float32":          # two roundings: float64 -> f32 -> bf16
+                v = float(np.float32(v))
+            sign = 0x8000 if math.copysign(1.0, v) < 0 else 0
+            m = abs(v)
+            if m and m != math.inf:
+                e = math.frexp(m)[1] - 1
+                if mode != "no_subnormal_floor":
+                    e = max(e, -126)
+                q = math.ldexp(1.0, e - 7)
+                r = m / q
+                if mode == "truncate":
+                    r = math.floor(r)
+                elif mode == "ties_away":
+                    r = math.floor(r + 0.5)
+                else:
+                    r = round(r)
+                m = r * q
+            if m >= math.ldexp(1.0, 128):
+                out[i] = sign | 0x7F80
+                continue
+            out[i] = sign | (int(np.array([m], dtype=np.float32).view(np.uint32)[0]) >> 16)
+        return out.reshape(np.shape(x))
+    return round_to_bf16_bits
+
+
+def _ulp_without_sign(a, b):
+    return np.abs(np.asarray(a, dtype=np.int64) - np.asarray(b, dtype=np.int64))
+
+
 MUTANTS = {
+    "bf16_round_truncates": ("round_to_bf16_bits", _round_variant("truncate")),
+    "bf16_round_ties_away": ("round_to_bf16_bits", _round_variant("ties_away")),
+    "bf16_round_twice_via_f32": ("round_to_bf16_bits", _round_variant("via_float32")),
+    "bf16_round_no_subnormals": ("round_to_bf16_bits", _round_variant("no_subnormal_floor")),
+    "ulp_distance_ignores_sign": ("bf16_ulp_distance", _ulp_without_sign),
     "gqa_head_modulo": ("attention", _attention_variant(group_of=lambda h, G, Hkv: h % Hkv)),
     "scale_dropped": ("attention", _attention_variant(use_scale=False)),
     "no_max_shift": ("attention", _attention_variant(shift=False)),
