@@ -70,13 +70,16 @@ typedef enum {
   PA_OK = 0,
   PA_ERR_INVALID_ARGUMENT = 1,
   PA_ERR_UNSUPPORTED = 2,
-  PA_ERR_LAUNCH = 3
+  PA_ERR_LAUNCH = 3,
+  PA_ERR_SCRATCH_LIMIT = 4
 } pa_status;
 
 typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype;
 
 #define PA_PAGE_SIZE 16
 #define PA_MAX_GQA_GROUP 16
+/* Size of the per-GPU scratch array of pa_chunk_attention_split_noalloc. */
+#define PA_SCRATCH_BYTES (64 * 1024 * 1024)
 
 /*
  * pa_reshape_and_cache — the slot-mapped cache write.
@@ -229,6 +232,36 @@ int pa_chunk_attention_split(void* out, const void* query, const void* k_cache,
                              int max_pages_per_seq, int64_t num_pages, float scale,
                              int partition_size, int max_num_partitions, float* partial_out,
                              float* partial_max, float* partial_sum, int dtype, void* stream);
+
+/*
+ * pa_chunk_attention_split_noalloc — pa_chunk_attention_split without the
+ * caller's workspace, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The split partials live in a fixed array of PA_SCRATCH_BYTES
+ * (64 MiB) per GPU, part of the library's device image, held until the
+ * process ends; its address is looked up once per device, on the first call
+ * with that device current.  The call allocates and frees nothing.
+ *
+ * Arguments, results and errors as for pa_chunk_attention_split, without
+ * partial_out / partial_max / partial_sum.  The partials take
+ * num_query_tokens * num_q_heads * max_num_partitions * (head_dim + 2) * 4
+ * bytes; a call that needs more than PA_SCRATCH_BYTES returns
+ * PA_ERR_SCRATCH_LIMIT and launches nothing (e.g. 64 sequences x 8 drafted
+ * tokens x 32 heads x 6 partitions at head_dim 128 take 51 MB).  Nothing in
+ * the array needs to start at any value: every partial the merge reads is
+ * written earlier in the same call.  Every call on one GPU shares that GPU's
+ * array: calls that may overlap on one GPU (different streams without
+ * ordering between them, or several host threads) race and give unspecified
+ * results; calls ordered on one stream are safe.
+ */
+int pa_chunk_attention_split_noalloc(void* out, const void* query, const void* k_cache,
+                                     const void* v_cache, const int32_t* block_tables,
+                                     const int32_t* context_lens, const int32_t* query_start,
+                                     int num_seqs, int num_query_tokens, int max_query_len,
+                                     int num_q_heads, int num_kv_heads, int head_dim,
+                                     int page_size, int max_pages_per_seq, int64_t num_pages,
+                                     float scale, int partition_size, int max_num_partitions,
+                                     int dtype, void* stream);
 
 /*
  * pa_decode_append — one decode step in one call: write each sequence's new

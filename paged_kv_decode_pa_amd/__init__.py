@@ -6,10 +6,12 @@ marshalling.  Build the library with ``python -m paged_kv_decode_pa_amd.build``.
 from ._lib import (  # noqa: F401
     LIB_PATH,
     PAGE_SIZE,
+    SCRATCH_BYTES,
     PaError,
     load,
     pa_chunk_attention,
     pa_chunk_attention_split,
+    pa_chunk_attention_split_noalloc,
     pa_decode,
     pa_decode_append,
     pa_decode_cascade,

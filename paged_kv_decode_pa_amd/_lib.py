@@ -18,6 +18,8 @@ PA_OK = 0
 PA_ERR_INVALID_ARGUMENT = 1
 PA_ERR_UNSUPPORTED = 2
 PA_ERR_LAUNCH = 3
+PA_ERR_SCRATCH_LIMIT = 4
+SCRATCH_BYTES = 64 * 1024 * 1024  # the per-GPU array of pa_chunk_attention_split_noalloc
 PA_DTYPE_F32 = 0
 PA_DTYPE_BF16 = 1
 PAGE_SIZE = 16
@@ -51,6 +53,10 @@ _SIGNATURES = {
                                  _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                  _i32, _i64, _f32, _i32, _i32, _c_void_p, _c_void_p, _c_void_p,
                                  _i32, _c_void_p],
+    "pa_chunk_attention_split_noalloc": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                         _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32,
+                                         _i32, _i32, _i32, _i64, _f32, _i32, _i32, _i32,
+                                         _c_void_p],
     "pa_decode_reduce": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
                          _i32, _i32, _i32, _c_void_p],
     "pa_export_pages": [_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _i32,
@@ -294,6 +300,29 @@ def pa_chunk_attention_split(out, query, k_cache, v_cache, block_tables, context
         block_tables.shape[1], k_cache.shape[0], float(scale), int(partition_size), P,
         _ptr(partial_out), _ptr(partial_max), _ptr(partial_sum), _dtype_code(query),
         _stream(stream)))
+
+
+def pa_chunk_attention_split_noalloc(out, query, k_cache, v_cache, block_tables, context_lens,
+                                     query_start, max_query_len, scale, partition_size,
+                                     max_num_partitions, stream=None) -> None:
+    """pa_chunk_attention_split with its partials in the library's fixed
+    per-GPU scratch array (SCRATCH_BYTES): the call allocates nothing.  Calls
+    that overlap on one GPU race; see include/pa.h."""
+    T, Hq, D = query.shape
+    B = context_lens.shape[0]
+    Hkv = k_cache.shape[1]
+    if k_cache.shape[2:] != (PAGE_SIZE, D) or v_cache.shape[1:] != (Hkv, D, PAGE_SIZE):
+        raise ValueError("pool shape does not match query")
+    if block_tables.shape[0] != B or tuple(query_start.shape) != (B + 1,):
+        raise ValueError("block_tables / query_start do not match the batch")
+    if out.shape != query.shape or out.dtype != query.dtype:
+        raise ValueError("out must match query")
+    lib = load()
+    _check("pa_chunk_attention_split_noalloc", lib.pa_chunk_attention_split_noalloc(
+        _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        _ptr(context_lens), _ptr(query_start), B, T, int(max_query_len), Hq, Hkv, D, PAGE_SIZE,
+        block_tables.shape[1], k_cache.shape[0], float(scale), int(partition_size),
+        int(max_num_partitions), _dtype_code(query), _stream(stream)))
 
 
 def _page_copy(name, buffer, k_cache, v_cache, page_ids, stream):

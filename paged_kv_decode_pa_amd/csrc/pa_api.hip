@@ -4,6 +4,8 @@
 #include <limits.h>
 #include <math.h>
 
+#include <mutex>
+
 #include "pa.h"
 #include "pa_device.hpp"
 
@@ -172,15 +174,43 @@ int page_copy_impl(bool export_dir, void* buffer, int64_t buffer_bytes, void* k_
   return err == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+// ------------------------------------------------------------------ scratch
+// Split partials of pa_chunk_attention_split_noalloc: one fixed array per
+// GPU, held until the process ends, so that call allocates nothing.  In host
+// code `scratch` names a host-side stand-in; its device address comes from
+// hipGetSymbolAddress, taken once per device (with that device current) and
+// kept per device.
+constexpr int64_t kScratchBytes = int64_t(PA_SCRATCH_BYTES);
+static __device__ __align__(256) unsigned char scratch[PA_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PA_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return PA_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
 // Multi-token attention, single pass (partition_size 0) or split-KV with the
-// merge in the same call.
+// merge in the same call; with use_scratch the split partials live in this
+// device's scratch array instead of the caller's buffers.
 int chunk_impl(void* out, const void* query, const void* k_cache, const void* v_cache,
                const int32_t* block_tables, const int32_t* context_lens,
                const int32_t* query_start, int num_seqs, int num_query_tokens, int max_query_len,
                int num_q_heads, int num_kv_heads, int head_dim, int page_size,
                int max_pages_per_seq, int64_t num_pages, float scale, int partition_size,
                int max_num_partitions, float* partial_out, float* partial_max,
-               float* partial_sum, int dtype, void* stream) {
+               float* partial_sum, int dtype, void* stream, bool use_scratch = false) {
   if (num_seqs < 0 || num_query_tokens < 0 || max_query_len < 0 || num_q_heads <= 0 ||
       num_kv_heads <= 0 || max_pages_per_seq <= 0 || num_pages <= 0)
     return PA_ERR_INVALID_ARGUMENT;
@@ -198,9 +228,14 @@ int chunk_impl(void* out, const void* query, const void* k_cache, const void* v_
   const bool split = partition_size > 0;
   if (split) {
     if (partition_size % PA_PAGE_SIZE != 0 || max_num_partitions < 1) return PA_ERR_INVALID_ARGUMENT;
-    if (!partial_out || !partial_max || !partial_sum || !aligned16(partial_out))
+    if (!use_scratch && (!partial_out || !partial_max || !partial_sum || !aligned16(partial_out)))
       return PA_ERR_INVALID_ARGUMENT;
   }
+  // Scratch layout: partial_out [T][Hq][P][D], then partial_max and
+  // partial_sum [T][Hq][P] (every part a multiple of 16 bytes from the start).
+  const int64_t scratch_rows = int64_t(num_query_tokens) * num_q_heads * max_num_partitions;
+  if (use_scratch && scratch_rows * (head_dim + 2) * int64_t(sizeof(float)) > kScratchBytes)
+    return PA_ERR_SCRATCH_LIMIT;
   const int64_t blocks = (int64_t(max_query_len) * group + 15) / 16;
   const int64_t per_wave = blocks < 4 ? (blocks > 0 ? blocks : 1) : 4;
   const int64_t groups = (blocks + per_wave - 1) / per_wave;
@@ -211,6 +246,13 @@ int chunk_impl(void* out, const void* query, const void* k_cache, const void* v_
       int64_t(num_seqs) * max_query_len * num_q_heads > INT_MAX)
     return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0) return PA_OK;
+  if (use_scratch) {
+    void* base = nullptr;
+    if (int st = scratch_of_current_device(&base)) return st;
+    partial_out = static_cast<float*>(base);
+    partial_max = partial_out + scratch_rows * head_dim;
+    partial_sum = partial_max + scratch_rows;
+  }
 
   pa::ChunkParams p;
   p.out = out;
@@ -396,6 +438,22 @@ int pa_chunk_attention_split(void* out, const void* query, const void* k_cache,
                     max_num_partitions, partial_out, partial_max, partial_sum, dtype, stream);
 }
 
+int pa_chunk_attention_split_noalloc(void* out, const void* query, const void* k_cache,
+                                     const void* v_cache, const int32_t* block_tables,
+                                     const int32_t* context_lens, const int32_t* query_start,
+                                     int num_seqs, int num_query_tokens, int max_query_len,
+                                     int num_q_heads, int num_kv_heads, int head_dim,
+                                     int page_size, int max_pages_per_seq, int64_t num_pages,
+                                     float scale, int partition_size, int max_num_partitions,
+                                     int dtype, void* stream) {
+  if (partition_size <= 0) return PA_ERR_INVALID_ARGUMENT;
+  return chunk_impl(out, query, k_cache, v_cache, block_tables, context_lens, query_start,
+                    num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads,
+                    head_dim, page_size, max_pages_per_seq, num_pages, scale, partition_size,
+                    max_num_partitions, nullptr, nullptr, nullptr, dtype, stream,
+                    /*use_scratch=*/true);
+}
+
 int pa_export_pages(void* buffer, int64_t buffer_bytes, const void* k_cache, const void* v_cache,
                     const int32_t* page_ids, int64_t num_ids, int num_kv_heads, int head_dim,
                     int page_size, int64_t num_pages, int dtype, void* stream) {
@@ -449,6 +507,7 @@ const char* pa_status_string(int status) {
     case PA_ERR_INVALID_ARGUMENT: return "PA_ERR_INVALID_ARGUMENT";
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
     case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH";
+    case PA_ERR_SCRATCH_LIMIT: return "PA_ERR_SCRATCH_LIMIT";
     default: return "PA_ERR_UNKNOWN";
   }
 }

@@ -248,6 +248,46 @@ def test_split_chunk_attention_empty_is_a_noop():
     assert lib.pa_chunk_attention_split(*split_chunk_args(num_query_tokens=0, max_query_len=0)) == OK
 
 
+def noalloc_chunk_args(**kw):
+    a = dict(out=P, query=P, k_cache=P, v_cache=P, block_tables=P, context_lens=P,
+             query_start=P, num_seqs=4, num_query_tokens=16, max_query_len=4, num_q_heads=32,
+             num_kv_heads=8, head_dim=128, page_size=16, max_pages_per_seq=8, num_pages=64,
+             scale=0.088, partition_size=64, max_num_partitions=2, dtype=BF16, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+NOALLOC_CASES = [
+    ("zero_partition", dict(partition_size=0), INVAL),
+    ("partition_not_page_multiple", dict(partition_size=40), INVAL),
+    ("zero_max_partitions", dict(max_num_partitions=0), INVAL),
+    ("null_query_start", dict(query_start=None), INVAL),
+    ("f32", dict(dtype=F32), UNSUP),
+    # 4096 tokens x 32 heads x 64 partitions x (128 + 2) floats = 4.4 GB
+    ("past_the_scratch_array", dict(num_seqs=64, num_query_tokens=4096, max_query_len=64,
+                                    max_num_partitions=64), _lib.PA_ERR_SCRATCH_LIMIT),
+    # one token x 8 heads x enough partitions to pass the array by under 8 rows
+    ("one_row_past", dict(num_seqs=1, num_query_tokens=1, max_query_len=1, num_q_heads=8,
+                          num_kv_heads=8,
+                          max_num_partitions=(_lib.SCRATCH_BYTES // (130 * 4)) // 8 + 1),
+     _lib.PA_ERR_SCRATCH_LIMIT),
+]
+
+
+@pytest.mark.parametrize("name,kw,want", NOALLOC_CASES, ids=[c[0] for c in NOALLOC_CASES])
+def test_noalloc_chunk_attention_rejects(name, kw, want):
+    assert pa.load().pa_chunk_attention_split_noalloc(*noalloc_chunk_args(**kw)) == want
+
+
+def test_noalloc_chunk_attention_empty_is_a_noop():
+    """No work, no scratch lookup and no HIP call (this host has no GPU)."""
+    lib = pa.load()
+    assert lib.pa_chunk_attention_split_noalloc(*noalloc_chunk_args(num_seqs=0)) == OK
+    assert lib.pa_chunk_attention_split_noalloc(
+        *noalloc_chunk_args(num_query_tokens=0, max_query_len=0)) == OK
+    assert pa.status_string(_lib.PA_ERR_SCRATCH_LIMIT) == "PA_ERR_SCRATCH_LIMIT"
+
+
 def test_chunk_attention_empty_is_a_noop():
     lib = pa.load()
     assert lib.pa_chunk_attention(*chunk_args(num_seqs=0)) == OK
