@@ -319,35 +319,7 @@ __device__ inline int longest_first(const ChunkParams& p, int rank, int lane) {
     len[c] = -1;  // past the batch
     if (c < nc && b < p.num_seqs) len[c] = min(max(p.context_lens[b], 0), cap);
   }
-  int top = 0;
-#pragma unroll
-  for (int c = 0; c < kPlanChunks; ++c) top = max(top, len[c]);
-#pragma unroll
-  for (int x = 1; x < 64; x <<= 1) top = max(top, __shfl_xor(top, x));
-  auto count_ge = [&](int t) {
-    int n = 0;
-#pragma unroll
-    for (int c = 0; c < kPlanChunks; ++c)
-      if (c < nc) n += __popcll(__ballot(len[c] >= t));
-    return n;
-  };
-  int lo = 0, hi = top + 1;  // count_ge(lo) > rank >= count_ge(hi)
-  while (hi - lo > 1) {
-    const int mid = lo + ((hi - lo) >> 1);
-    if (count_ge(mid) > rank) lo = mid; else hi = mid;
-  }
-  int k = rank - count_ge(lo + 1);  // rank among the sequences of length lo
-  int seq = -1;
-#pragma unroll
-  for (int c = 0; c < kPlanChunks; ++c) {
-    if (c < nc) {
-      const uint64_t m = __ballot(len[c] == lo);
-      const int n = __popcll(m);
-      if (seq < 0 && k >= 0 && k < n) seq = 64 * c + kth_set_lane(m, k, lane);
-      k -= n;
-    }
-  }
-  seq = __builtin_amdgcn_readfirstlane(seq);
+  const int seq = seq_of_rank<kPlanChunks>(len, nc, rank, lane);
   return seq >= 0 ? seq : rank;
 }
 
@@ -705,7 +677,10 @@ __global__ __launch_bounds__(kBlock) void cascade_kernel(PrefixParams q, DecodeP
   }
   int seq, kvh, part;
   if (!unit_of(p, b - q.num_units, seq, kvh, part)) return;
-  whole_unit<D>(p, seq, kvh, part, smem);
+  __builtin_amdgcn_s_setprio(3);  // lowered before the page stream starts
+  // Cached loads: the nontemporal hint on these units (a sequence's own
+  // partitions, past its group's shared prefix) measured 5% slower.
+  whole_unit<D>(p, seq, kvh, part, smem, /*shared=*/true);
 }
 
 template <int D>

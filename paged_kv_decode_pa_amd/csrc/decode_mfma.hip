@@ -20,6 +20,10 @@ template <int D, int NC>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   const int u = blockIdx.x;
   if (u >= p.num_units) return;
+  // The prologue (the unit plan and the first loads) runs at raised priority:
+  // a wave's SIMD otherwise issues for its older, streaming waves first, and a
+  // younger wave's page ids then arrive only when those have finished.
+  __builtin_amdgcn_s_setprio(3);
   const int kvh = u % p.num_kv_heads;
   const int useq = u / p.num_kv_heads;
   const int lane = threadIdx.x;
@@ -73,6 +77,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   }
   writes = writes && nt.valid(p);
   ps.count = hi - lo;
+  __builtin_amdgcn_s_setprio(0);
   wa.run(ps, lo, L, lane, sharing.shared(p, seq, lane), writes, nt);
   if (writes) nt.store(p, kvh, lane);
 
@@ -99,16 +104,38 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
 
 // ---------------------------------------------------------------- single pass
 // Unit = (sequence, kv head), four waves; wave w takes pages w, w+4, ...
+// In batches of up to 1024 sequences, unit slot i (kv head fastest) takes the
+// sequence of rank snake_rank(i) by length, longest first, so each compute
+// unit's units add up to about the same number of pages, and a sequence that
+// shares no first page with another streams with the nontemporal hint
+// (larger batches: batch order, cached loads).
 // With partitions (the four-wave split-KV units, chosen when the batch has
 // few units for the machine, as a shared-prefix step's suffixes do), unit =
 // (sequence, partition, kv head) over the partition's pages, and the merged
 // state is written as that partition's partial.
-template <int D>
+template <int D, int NC>
 __global__ __launch_bounds__(kBlock) void decode_whole_kernel(DecodeParams p) {
   extern __shared__ float smem[];
   int seq, kvh, part;
   if (!unit_of(p, blockIdx.x, seq, kvh, part)) return;
-  whole_unit<D>(p, seq, kvh, part, smem);
+  __builtin_amdgcn_s_setprio(3);  // lowered before the page stream starts
+  bool shared = true;
+  if constexpr (NC > 0) {
+    if (p.pages_per_partition == 0) {
+      const int lane = threadIdx.x & 63;
+      FirstPages<NC> fp;
+      fp.request(p, lane);
+      const int cap = min(p.max_pages_per_seq, (1 << 30) / kPage - 1) * kPage;
+      int len[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        len[c] = 64 * c + lane < p.num_seqs ? min(max(fp.len[c], 0), cap) : -1;
+      const int s = seq_of_rank<NC>(len, NC, snake_rank(seq, p.snake_period, p.num_seqs), lane);
+      seq = s >= 0 ? s : seq;
+      shared = fp.shared(p, seq, lane);
+    }
+  }
+  whole_unit<D>(p, seq, kvh, part, smem, shared);
 }
 
 template <int D>
@@ -124,7 +151,13 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
     }
   } else {
     const size_t lds = merge_lds_bytes(p.group, D);
-    decode_whole_kernel<D><<<dim3(decode_grid(p.num_units)), kBlock, lds, stream>>>(p);
+    const dim3 grid(decode_grid(p.num_units));
+    switch (p.pages_per_partition == 0 ? plan_chunks_for(p.num_seqs) : 0) {
+      case 1: decode_whole_kernel<D, 1><<<grid, kBlock, lds, stream>>>(p); break;
+      case 4: decode_whole_kernel<D, 4><<<grid, kBlock, lds, stream>>>(p); break;
+      case kPlanChunks: decode_whole_kernel<D, kPlanChunks><<<grid, kBlock, lds, stream>>>(p); break;
+      default: decode_whole_kernel<D, 0><<<grid, kBlock, lds, stream>>>(p); break;
+    }
   }
   return hipGetLastError();
 }

@@ -4,6 +4,7 @@
 #include <limits.h>
 #include <math.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "pa.h"
@@ -48,6 +49,23 @@ int check_common(int head_dim, int page_size, int dtype) {
 }
 
 enum class DecodeKernel { kAuto, kValu };
+
+// Compute units of the current device, looked up once per device (0 when
+// unknown): the single-pass decode's unit order pairs sequences per compute
+// unit.
+constexpr int kMaxDevicesCached = 64;
+std::atomic<int> g_device_cus[kMaxDevicesCached];
+
+int device_compute_units() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevicesCached) return 0;
+  int n = g_device_cus[dev].load(std::memory_order_relaxed);
+  if (n == 0 &&
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      n > 0)
+    g_device_cus[dev].store(n, std::memory_order_relaxed);
+  return n > 0 ? n : 0;
+}
 
 // Checks a decode call's host arguments and fills its launch parameters;
 // *empty when there is nothing to launch.  new_key == NULL: decode only.
@@ -117,6 +135,7 @@ int decode_setup(DecodeKernel which, void* out, const void* query, const void* k
   p.num_units = int(units);
   p.first_partition = first_partition;
   p.four_wave_units = four_wave_units && split;
+  p.snake_period = 0;
   mfma = dtype == PA_DTYPE_BF16 && which == DecodeKernel::kAuto;
   p.new_key = mfma ? new_key : nullptr;
   p.new_value = mfma ? new_value : nullptr;
@@ -140,6 +159,10 @@ int decode_impl(DecodeKernel which, void* out, const void* query, const void* k_
                             new_key, new_value, new_slots, nullptr, false, 0, p, mfma, empty))
     return st;
   if (empty) return PA_OK;
+  if (mfma && partition_size == 0) {
+    const int cus = device_compute_units();
+    p.snake_period = cus > 0 ? (cus / num_kv_heads > 0 ? cus / num_kv_heads : 1) : 0;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = dtype == PA_DTYPE_BF16;
   if (new_key && !mfma) {

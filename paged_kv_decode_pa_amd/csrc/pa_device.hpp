@@ -49,6 +49,9 @@ struct DecodeParams {
   // Split-KV with four waves per (sequence, partition, kv head) unit instead
   // of one: for batches with few units for the machine.
   bool four_wave_units;
+  // Single pass: sequences per round of units over the compute units (see
+  // snake_rank); 0 keeps the batch order.
+  int snake_period;
 };
 
 // Split-KV partials of the pages a group of sequences shares from position 0:

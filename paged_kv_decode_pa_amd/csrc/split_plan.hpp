@@ -170,6 +170,59 @@ __device__ bool split_unit(const Params& p, int useq, int lane, int& seq, int& p
   return seq >= 0;
 }
 
+// The sequence of rank `rank` when the batch is ordered by context length,
+// longest first, ties in batch order.  len[c] is the length of sequence
+// 64c + lane (-1 past the batch) for the first nc chunks.  The rank's length
+// comes from a binary search on the count of lengths at or above a threshold
+// (wave ballots), then the tie by its batch order.  -1 for a rank past the
+// batch.
+template <int NC>
+__device__ inline int seq_of_rank(const int (&len)[NC], int nc, int rank, int lane) {
+  int top = 0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) top = max(top, len[c]);
+#pragma unroll
+  for (int x = 1; x < 64; x <<= 1) top = max(top, __shfl_xor(top, x));
+  auto count_ge = [&](int t) {
+    int n = 0;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      if (c < nc) n += __popcll(__ballot(len[c] >= t));
+    return n;
+  };
+  int lo = 0, hi = top + 1;  // count_ge(lo) > rank >= count_ge(hi)
+  while (hi - lo > 1) {
+    const int mid = lo + ((hi - lo) >> 1);
+    if (count_ge(mid) > rank) lo = mid; else hi = mid;
+  }
+  int k = rank - count_ge(lo + 1);  // rank among the sequences of length lo
+  int seq = -1;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (c < nc) {
+      const uint64_t m = __ballot(len[c] == lo);
+      const int n = __popcll(m);
+      if (seq < 0 && k >= 0 && k < n) seq = 64 * c + kth_set_lane(m, k, lane);
+      k -= n;
+    }
+  }
+  return __builtin_amdgcn_readfirstlane(seq);
+}
+
+// Single-pass units go to the compute units in grid order, one each per
+// round of `period` sequences (the machine's compute units divided by the kv
+// heads, which vary fastest), and a unit shares its compute unit with the
+// units one, two, ... rounds later.  Ranks run forward in even rounds and
+// backward in odd ones, so a compute unit that takes a long sequence in one
+// round takes a short one in the next and the totals even out.  period 0:
+// rank = slot.
+__host__ __device__ inline int snake_rank(int slot, int period, int num_seqs) {
+  if (period <= 0) return slot;
+  const int k = slot / period, j = slot % period;
+  const int m = min(period, num_seqs - k * period);  // sequences in this round
+  return k * period + ((k & 1) ? m - 1 - j : j);
+}
+
 // Batch-size buckets of the device-side plan and the sharing test: their
 // arrays are sized for NC * 64 sequences, NC in {1, 4, 16}, picked by the
 // host.  NC = 0 (batches above 1024 sequences) does without both: a plain

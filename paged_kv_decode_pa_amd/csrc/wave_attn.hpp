@@ -224,10 +224,13 @@ __device__ inline PageStream<D> make_stream(const DecodeParams& p, int seq, int 
 // Four-wave unit (sequence, partition, kv head) -- or (sequence, kv head)
 // over the whole context when pages_per_partition is 0; wave w takes pages
 // w, w+4, ... of the unit, and the four states merge through LDS into the
-// output row or the partition's partial.  Every thread of the 256-thread
-// block must call it.
+// output row or the partition's partial.  `shared`: some page the unit reads
+// may also be read by another sequence (cached loads); otherwise its pages
+// stream with the nontemporal hint.  Every thread of the 256-thread block
+// must call it.
 template <int D>
-__device__ inline void whole_unit(const DecodeParams& p, int seq, int kvh, int part, float* smem) {
+__device__ inline void whole_unit(const DecodeParams& p, int seq, int kvh, int part, float* smem,
+                                  bool shared) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, j = lane >> 4;
@@ -260,10 +263,8 @@ __device__ inline void whole_unit(const DecodeParams& p, int seq, int kvh, int p
   const int n = min((L + kPage - 1) / kPage, p.max_pages_per_seq);
   const bool writes = appends && hi == n && (hi - 1 - lo) % kWaves == w && nt.valid(p);
   ps.count = w < hi - lo ? (hi - lo - w + kWaves - 1) / kWaves : 0;
-  // Cached loads throughout: with four waves per unit this kernel runs far
-  // fewer waves than the split one, and the nontemporal hint measured up to
-  // 25% slower here (long contexts of the 256-sequence batch).
-  wa.run(ps, lo + w, L, lane, /*shared=*/true, writes, nt);
+  __builtin_amdgcn_s_setprio(0);  // the prologue ran at raised priority
+  wa.run(ps, lo + w, L, lane, shared, writes, nt);
   if (writes) nt.store(p, kvh, lane);
 
   MergeLds lds(smem);

@@ -121,7 +121,8 @@ def check_exact(out, want_bits, what):
 
 
 def _partitions(cid):
-    return sorted({0, config_by_id(cid).bench_partition_size, 2048, 4096})
+    extra = {768} if cid == 2 else set()
+    return sorted({0, config_by_id(cid).bench_partition_size, 2048, 4096} | extra)
 
 
 DECODE_CASES = [(cid, mode, ps) for cid in (2, 4, 5) for mode in ("flat", "comb")
@@ -139,13 +140,14 @@ def test_decode_exact(cid, mode, ps):
 @pytest.mark.parametrize("cid,mode", [(2, "flat"), (2, "comb"), (5, "comb")])
 def test_decode_valu_exact(cid, mode):
     dev = exact_device(cid, mode)
-    for ps in (0, config_by_id(cid).bench_partition_size):
+    for ps in sorted({0, config_by_id(cid).bench_partition_size or 768}):
         say(f"[exact] pa_decode_valu config {cid} {mode} partition {ps}")
         check_exact(dev.decode(ps, "valu"), exact_reference_bits(cid, mode), "pa_decode_valu")
 
 
 APPEND_CASES = [(cid, mode, ps) for cid in (2, 4, 5) for mode in ("flat", "comb")
-                for ps in sorted({0, config_by_id(cid).bench_partition_size, 4096})]
+                for ps in sorted({0, config_by_id(cid).bench_partition_size, 4096}
+                                 | ({768} if cid == 2 else set()))]
 
 
 @pytest.mark.parametrize("cid,mode,ps", APPEND_CASES,

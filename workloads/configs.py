@@ -75,7 +75,7 @@ CONFIGS = [
     DecodeConfig(2, "llama3_8b_bf16", 64, 32, 8, 128, "bf16",
                  "batch 64, 32 q / 8 kv heads, D=128, bf16, lengths U[512,4096], "
                  "pages scattered in a pool of 1.25x need",
-                 bench_partition_size=768),
+                 bench_partition_size=0),
     DecodeConfig(3, "prefix_reuse_bf16", 128, 32, 8, 128, "bf16",
                  "batch 128 = 8 groups x 16 sharing a 2048-token prefix, private "
                  "suffixes U[64,512], 32 q / 8 kv heads, D=128, bf16",
