@@ -16,7 +16,7 @@ LIB = os.path.join(PKG, "libpa.so")
 PAGER_LIB = os.path.join(PKG, "libpa_pager.so")
 PAGER_SOURCES = ["pager.cpp"]
 SOURCES = ["pa_api.hip", "reshape_and_cache.hip", "decode_mfma.hip", "decode_valu.hip",
-           "decode_reduce.hip", "chunk_mfma.hip", "page_transfer.hip"]
+           "decode_reduce.hip", "chunk_mfma.hip", "chunk_lds.hip", "page_transfer.hip"]
 ARCH = "gfx950"
 
 

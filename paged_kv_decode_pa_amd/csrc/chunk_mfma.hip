@@ -301,28 +301,6 @@ __host__ __device__ inline size_t chunk_query_lds_bytes(int head_dim, int nb) {
   return chunk_query_in_lds(nb) ? size_t(nb) * (head_dim / 32) * 64 * 16 : 0;
 }
 
-// The sequence of rank `rank` when the batch is ordered by context length
-// (clamped to the table), longest first, ties in batch order; a batch above
-// kPlanMaxSeqs keeps its order.  Units are dispatched in grid order, so the
-// long sequences' units start first and the short ones fill in behind them,
-// instead of a long sequence's units starting late and setting the end.
-// The rank's length is found by a binary search on the count of lengths at
-// or above a threshold (wave ballots), then the tie by its batch order.
-__device__ inline int longest_first(const ChunkParams& p, int rank, int lane) {
-  if (p.num_seqs > kPlanMaxSeqs) return rank;
-  const int nc = (p.num_seqs + 63) >> 6;
-  const int cap = min(p.max_pages_per_seq, (1 << 30) / kPage - 1) * kPage;
-  int len[kPlanChunks];
-#pragma unroll
-  for (int c = 0; c < kPlanChunks; ++c) {
-    const int b = 64 * c + lane;
-    len[c] = -1;  // past the batch
-    if (c < nc && b < p.num_seqs) len[c] = min(max(p.context_lens[b], 0), cap);
-  }
-  const int seq = seq_of_rank<kPlanChunks>(len, nc, rank, lane);
-  return seq >= 0 ? seq : rank;
-}
-
 template <int D, int NB>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(NB >= 3 ? 2 : 1)))
 void chunk_attention_kernel(ChunkParams p) {

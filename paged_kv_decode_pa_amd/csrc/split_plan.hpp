@@ -233,6 +233,32 @@ __host__ __device__ constexpr int plan_chunks_for(int num_seqs) {
   return num_seqs <= 64 ? 1 : num_seqs <= 256 ? 4 : num_seqs <= kPlanMaxSeqs ? kPlanChunks : 0;
 }
 
+// The sequence of rank `rank` when the batch is ordered by context length
+// (clamped to the table), longest first, ties in batch order; a batch above
+// kPlanMaxSeqs keeps its order.  Units are dispatched in grid order, so the
+// long sequences' units start first and the short ones fill in behind them,
+// instead of a long sequence's units starting late and setting the end.
+// The rank's length is found by a binary search on the count of lengths at
+// or above a threshold (wave ballots), then the tie by its batch order.
+template <class Params>
+__device__ inline int longest_first(const Params& p, int rank, int lane) {
+  if (p.num_seqs > kPlanMaxSeqs) return rank;
+  const int nc = (p.num_seqs + 63) >> 6;
+  const int cap = min(p.max_pages_per_seq, (1 << 30) / kPage - 1) * kPage;
+  // The loads go out together, unconditionally (a lane past the batch
+  // re-reads the last sequence): under a branch, the compiler waits for each
+  // load before the next.
+  int len[kPlanChunks];
+#pragma unroll
+  for (int c = 0; c < kPlanChunks; ++c)
+    len[c] = p.context_lens[min(64 * c + lane, p.num_seqs - 1)];
+#pragma unroll
+  for (int c = 0; c < kPlanChunks; ++c)
+    len[c] = 64 * c + lane < p.num_seqs ? min(max(len[c], 0), cap) : -1;  // -1: past the batch
+  const int seq = seq_of_rank<kPlanChunks>(len, nc, rank, lane);
+  return seq >= 0 ? seq : rank;
+}
+
 // The sharing test of sequence `seq`: its loads are issued by request(), the
 // answer is read by shared() after other loads have been issued.
 template <int NC>
