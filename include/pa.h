@@ -186,7 +186,11 @@ int pa_decode(void* out, const void* query, const void* k_cache, const void* v_c
  *                  sequence with no new token has no rows).
  *   the rest       as in pa_decode (pools, block tables, context lengths,
  *                  scale, page size).
- * Results are deterministic and do not depend on page placement.  A sequence
+ * Results are deterministic and do not depend on page placement.  With
+ * max_query_len * (num_q_heads / num_kv_heads) above 64 a kernel that stages
+ * K/V in LDS for 128 or 256 columns at a time runs instead of the 16-column
+ * one: the same results to rounding, so bits can change with max_query_len
+ * across that bound.  A sequence
  * whose q_len_b exceeds L_b gets unspecified rows, and one whose rows fall
  * outside [0, num_query_tokens) gets none written (no fault either way).  bf16 only:
  * PA_DTYPE_F32 returns PA_ERR_UNSUPPORTED.  max_query_len above

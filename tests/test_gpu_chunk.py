@@ -15,6 +15,8 @@ from workloads import make_chunk_queries, make_custom_workload
 
 pytestmark = pytest.mark.gpu
 
+LDS_MIN_COLUMNS = 64  # max_query_len * group above this: the LDS-staged kernel
+
 
 def run_chunk(dev, query, query_start, max_q=None):
     wl = dev.wl
@@ -70,8 +72,15 @@ def test_chunk_matches_oracle(lens, q_lens, Hq, Hkv, D):
     say(f"    max abs err {err:.3e}")
     assert err <= TOL["bf16"]
     # A looser bound on q_len changes how many column blocks a wave carries
-    # and adds units that exit at once; each column's arithmetic is the same.
-    assert np.array_equal(bits_of(run_chunk(dev, query, qs, max_q=int(qs[-1]))), bits_of(got))
+    # and adds units that exit at once; each column's arithmetic is the same
+    # as long as the bound keeps the same kernel (past 64 columns per kv
+    # head the LDS-staged kernel runs, with its own rounding order).
+    loose = run_chunk(dev, query, qs, max_q=int(qs[-1]))
+    G = Hq // Hkv
+    if (max(q_lens) * G > LDS_MIN_COLUMNS) == (int(qs[-1]) * G > LDS_MIN_COLUMNS):
+        assert np.array_equal(bits_of(loose), bits_of(got))
+    else:
+        assert max_err(loose, ref) <= TOL["bf16"]
 
 
 def test_spec_decode_batch_at_config_2_shape():
