@@ -44,6 +44,12 @@ CHUNK_KERNEL_SOURCES = ["paged_kv_decode_pa_amd/csrc/chunk_mfma.hip",
                         "paged_kv_decode_pa_amd/csrc/wave_attn.hpp",
                         "paged_kv_decode_pa_amd/csrc/page_stream.hpp",
                         "paged_kv_decode_pa_amd/csrc/pa_device.hpp"]
+# The multi-token kernel that stages K/V in LDS (more than 64 columns per kv head).
+CHUNK_LDS_KERNEL_SOURCES = ["paged_kv_decode_pa_amd/csrc/chunk_lds.hip",
+                            "paged_kv_decode_pa_amd/csrc/split_plan.hpp",
+                            "paged_kv_decode_pa_amd/csrc/page_stream.hpp",
+                            "paged_kv_decode_pa_amd/csrc/pa_device.hpp"]
+CHUNK_LDS_MIN_COLUMNS = 65  # max_query_len * (q heads per kv head) from which it runs
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 # --chunk default: split-KV (pa_chunk_attention_split) at this partition size up
 # to this many new tokens per sequence, the single pass above (measured on the
@@ -193,7 +199,7 @@ def copy_calibration(dev):
     torch.cuda.synchronize()
 
 
-def run_config(cid, args, headline):
+def run_config(cid, args):
     import torch
 
     import paged_kv_decode_pa_amd as pa
@@ -421,7 +427,7 @@ def run_config(cid, args, headline):
             "mean_launch_us": round(t_dec * 1e6, 2),
         },
     }
-    if headline and not args.no_cpu_baseline:
+    if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, nb, t_step)
     return line
 
@@ -556,7 +562,10 @@ def run_chunk_config(cid, args):
              "frac": round(hbm_frac, 4)} if bound == "hbm" else
             {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
              "unit": "TFLOP/s", "frac": round(mfma_frac, 4)})
-    kv = read_profile_kv(f"traffic_chunk_attention_cfg{cid}_q{q}.txt", CHUNK_KERNEL_SOURCES)
+    lds = not cps and q * (Hq // Hkv) >= CHUNK_LDS_MIN_COLUMNS
+    lds_waves = 8 if q * (Hq // Hkv) > 128 else 4
+    kv = read_profile_kv(f"traffic_chunk_attention_cfg{cid}_q{q}.txt",
+                         CHUNK_LDS_KERNEL_SOURCES if lds else CHUNK_KERNEL_SOURCES)
     traffic = None
     if kv is not None and not args.unshared and int(kv.get("partition_size", 0)) == cps:
         try:
@@ -565,7 +574,9 @@ def run_chunk_config(cid, args):
             traffic = None
     roof.update({"traffic": traffic,
                  "kernel": (f"chunk_split_kernel<{D}> + decode_reduce_kernel (one call, "
-                            f"{cps}-token partitions)" if cps else f"chunk_attention_kernel<{D}>"),
+                            f"{cps}-token partitions)" if cps else
+                            f"chunk_lds_kernel<{D}, {lds_waves}>" if lds else
+                            f"chunk_attention_kernel<{D}>"),
                  "algorithmic_bytes_per_launch": nb["kernel"], "flops_per_launch": nb["flops"],
                  "hbm_gbs": round(gbs, 1), "bf16_tflops": round(tflops, 2),
                  "mean_launch_us": round(t_attn * 1e6, 2)})
@@ -850,8 +861,8 @@ def main():
         return
     others = [c for c in (1, 2, 3, 4, 5) if c != args.config] if args.all else []
     for cid in others:
-        print(json.dumps(run_config(cid, args, headline=False)), file=sys.stderr, flush=True)
-    print(json.dumps(run_config(args.config, args, headline=True)), flush=True)
+        print(json.dumps(run_config(cid, args)), file=sys.stderr, flush=True)
+    print(json.dumps(run_config(args.config, args)), flush=True)
 
 
 if __name__ == "__main__":

@@ -431,6 +431,9 @@ __global__ __launch_bounds__(64) void chunk_split_kernel(ChunkParams p) {
   const int r = lane & 15, j = lane >> 4;
   const int G = p.group;
 
+  // The sharing test's loads depend on nothing: they go out with the plan's.
+  SharingTest<NC> sharing;
+  sharing.request(p, lane);
   int seq, part, seq_pages = 0;
   if constexpr (NC > 0) {
     if (!split_unit<NC>(p, useq, lane, seq, part, seq_pages)) return;
@@ -441,10 +444,8 @@ __global__ __launch_bounds__(64) void chunk_split_kernel(ChunkParams p) {
   seq = __builtin_amdgcn_readfirstlane(seq);
   part = __builtin_amdgcn_readfirstlane(part);
 
-  // Issued together before any of them returns: the sharing test, the token
-  // offsets, the length and the partition's page ids.
-  SharingTest<NC> sharing;
-  sharing.request(p, lane);
+  // Issued together before any of them returns: the token offsets, the
+  // length and the partition's page ids.
   const int qa = p.query_start[seq];
   const int qb = p.query_start[seq + 1];
   const int L_raw = p.context_lens[seq];

@@ -30,6 +30,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   const int r = lane & 15, j = lane >> 4;
   const int G = p.group;
 
+  // The sharing test's loads (column 0 of every block-table row) depend on
+  // nothing: they go out with the plan's length loads.
+  SharingTest<NC> sharing;
+  sharing.request(p, lane);
   int seq, part, seq_pages = 0;
   if constexpr (NC > 0) {
     if (!split_unit<NC>(p, useq, lane, seq, part, seq_pages)) return;
@@ -42,8 +46,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   part = __builtin_amdgcn_readfirstlane(part);
 
   // Issued together before any of them returns: the new token (when this
-  // partition holds the sequence's last page and the launch appends), the
-  // sharing test, length, page ids, query.
+  // partition holds the sequence's last page and the launch appends), length,
+  // page ids, query.
   const bool appends = p.new_key != nullptr;
   bool writes = false;
   NewToken<D> nt;
@@ -51,8 +55,6 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
     writes = appends && (part + 1) * p.pages_per_partition >= seq_pages;
     if (writes) nt.request(p, seq, kvh, lane);
   }
-  SharingTest<NC> sharing;
-  sharing.request(p, lane);
   const int lo = part * p.pages_per_partition;
   const int row_end = min(lo + p.pages_per_partition, p.max_pages_per_seq);
   PageStream<D> ps = make_stream<D>(p, seq, kvh, lo, 1, row_end, lane);
@@ -108,7 +110,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
 // sequence of rank snake_rank(i) by length, longest first, so each compute
 // unit's units add up to about the same number of pages, and a sequence that
 // shares no first page with another streams with the nontemporal hint
-// (larger batches: batch order, cached loads).
+// (larger batches: batch order, cached loads).  A batch in which neighbours
+// share their first page keeps batch order: a prefix group's units then run
+// together and read the shared pages through one L2 while they stay there.
 // With partitions (the four-wave split-KV units, chosen when the batch has
 // few units for the machine, as a shared-prefix step's suffixes do), unit =
 // (sequence, partition, kv head) over the partition's pages, and the merged
@@ -130,8 +134,10 @@ __global__ __launch_bounds__(kBlock) void decode_whole_kernel(DecodeParams p) {
 #pragma unroll
       for (int c = 0; c < NC; ++c)
         len[c] = 64 * c + lane < p.num_seqs ? min(max(fp.len[c], 0), cap) : -1;
-      const int s = seq_of_rank<NC>(len, NC, snake_rank(seq, p.snake_period, p.num_seqs), lane);
-      seq = s >= 0 ? s : seq;
+      if (!fp.adjacent_shared(p, lane)) {
+        const int s = seq_of_rank<NC>(len, NC, snake_rank(seq, p.snake_period, p.num_seqs), lane);
+        seq = s >= 0 ? s : seq;
+      }
       shared = fp.shared(p, seq, lane);
     }
   }

@@ -19,11 +19,13 @@ namespace {
 constexpr int kReduceWaves = 4;  // (sequence, head) rows per workgroup
 constexpr int kGroup = 16;       // partitions per register set (a chunk holds 64 / kGroup sets)
 
-__device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int x = 1; x < 64; x <<= 1) v = fmaxf(v, __shfl_xor(v, x));
-  return v;
-}
+// Wavefront max and sum from the device library (cross-lane moves within the
+// vector unit, in a fixed order): the max is exact in any order, and the sum's
+// fixed order keeps the merge deterministic.
+extern "C" __device__ __attribute__((const)) float __ockl_wfred_max_f32(float);
+extern "C" __device__ __attribute__((const)) float __ockl_wfred_add_f32(float);
+
+__device__ inline float wave_max(float v) { return __ockl_wfred_max_f32(v); }
 
 template <int D>
 struct RowSet {
@@ -122,10 +124,9 @@ __global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_kernel(
       b.use(acc, w, g + 1, n);
     }
   }
-  // Denominator: lanes hold disjoint partitions; a butterfly sum in a fixed
-  // order gives every lane the same total.
-#pragma unroll
-  for (int x = 1; x < 64; x <<= 1) wsum += __shfl_xor(wsum, x);
+  // Denominator: lanes hold disjoint partitions; the wavefront sum (a fixed
+  // order) gives every lane the same total.
+  wsum = __ockl_wfred_add_f32(wsum);
 #pragma unroll
   for (int i = 0; i < VD; ++i)
     Elem<OutT>::store(out, size_t(row) * D + lane + 64 * i, n > 0 ? acc[i] / wsum : 0.f);

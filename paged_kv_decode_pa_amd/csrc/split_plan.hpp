@@ -10,11 +10,14 @@ namespace pa {
 
 constexpr int kPlanChunks = 16;  // batches up to 1024 sequences use the unit plan
 
-__device__ inline int wave_sum(int v) {
-#pragma unroll
-  for (int x = 1; x < 64; x <<= 1) v += __shfl_xor(v, x);
-  return v;
-}
+// Whole-wave sums and maxima through the device library's wavefront
+// reductions (cross-lane moves within the vector unit), not six LDS-routed
+// shuffles: the unit plan chains several of them before a wave's first load.
+extern "C" __device__ __attribute__((const)) int __ockl_wfred_add_i32(int);
+extern "C" __device__ __attribute__((const)) int __ockl_wfred_max_i32(int);
+
+__device__ inline int wave_sum(int v) { return __ockl_wfred_add_i32(v); }
+__device__ inline int wave_max_i32(int v) { return __ockl_wfred_max_i32(v); }
 
 // Index (within its 64-lane chunk) of the k-th set bit of a wave ballot.
 __device__ inline int kth_set_lane(uint64_t mask, int k, int lane) {
@@ -80,6 +83,24 @@ struct FirstPages {
     for (int c = 0; c < NC; ++c)
       first[c] = (64 * c + lane < p.num_seqs && len[c] > 0) ? fid[c] : -1;
     return first_page_shared<NC>(first, seq);
+  }
+  // Whether two sequences next to each other in the batch share their first
+  // page (a prefix group laid out contiguously, as a scheduler batches the
+  // requests of one prompt): then batch order keeps a group's units together
+  // in time, and the second reader of a page finds it in L2.
+  template <class Params>
+  __device__ bool adjacent_shared(const Params& p, int lane) const {
+    uint64_t hits = 0;
+    int last = -1;  // first page of sequence 64c - 1
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int f = (64 * c + lane < p.num_seqs && len[c] > 0) ? fid[c] : -1;
+      int prev = __shfl_up(f, 1);
+      if (lane == 0) prev = last;
+      hits |= __ballot(f >= 0 && f == prev);
+      last = __builtin_amdgcn_readlane(f, 63);
+    }
+    return hits != 0;
   }
 };
 
@@ -149,10 +170,24 @@ __device__ bool split_unit(const Params& p, int useq, int lane, int& seq, int& p
     int psize[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) psize[c] = hasp[c] ? pages[c] - (pages[c] / PP) * PP : 0;
-    for (int sz = PP - 1; sz >= 1 && seq < 0; --sz) {
+    auto count_ge = [&](int t) {  // partly filled partitions of at least t pages
+      int n = 0;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) n += __popcll(__ballot(psize[c] >= t));
+      return n;
+    };
+    if (k < part_total) {
+      // Unit k's size: the sz in [1, PP) with count_ge(sz + 1) <= k < count_ge(sz),
+      // by bisection (a scan over the sizes costs PP rounds of ballots).
+      int lo = 1, hi = PP;  // count_ge(lo) = part_total > k >= 0 = count_ge(hi)
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (count_ge(mid) > k) lo = mid; else hi = mid;
+      }
+      k -= count_ge(lo + 1);  // rank among the partitions of lo pages, in batch order
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const uint64_t m = __ballot(hasp[c] != 0 && psize[c] == sz);
+        const uint64_t m = __ballot(psize[c] == lo);
         const int n = __popcll(m);
         if (seq < 0 && k < n && k >= 0) {
           seq = 64 * c + kth_set_lane(m, k, lane);
@@ -181,8 +216,7 @@ __device__ inline int seq_of_rank(const int (&len)[NC], int nc, int rank, int la
   int top = 0;
 #pragma unroll
   for (int c = 0; c < NC; ++c) top = max(top, len[c]);
-#pragma unroll
-  for (int x = 1; x < 64; x <<= 1) top = max(top, __shfl_xor(top, x));
+  top = wave_max_i32(top);
   auto count_ge = [&](int t) {
     int n = 0;
 #pragma unroll

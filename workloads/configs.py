@@ -88,7 +88,7 @@ CONFIGS = [
     DecodeConfig(5, "llama70b_tp8_share_bf16", 256, 8, 1, 128, "bf16",
                  "batch 256, 8 q / 1 kv head, D=128, bf16, lengths log-uniform "
                  "[128,8192] with 25% of sequences at length <= 32",
-                 bench_partition_size=256),
+                 bench_partition_size=512),
 ]
 
 
