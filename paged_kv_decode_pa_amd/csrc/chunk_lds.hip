@@ -3,12 +3,12 @@
 //
 // Where chunk_attention_kernel splits a sequence's pages over four waves and
 // has every wave carry up to 64 columns, this kernel splits the columns:
-// unit = (sequence, kv head, group of 128 columns), four waves, wave w owns
-// 32 columns (column c = token * group + head, as there) and walks every key
-// position its columns can see.  The K and V of each 32-key step (two pages)
-// are read from HBM once per unit by all 256 threads, staged in LDS (double
-// buffered, two steps of loads in flight in registers) and read by the four
-// waves from there.
+// unit = (sequence, kv head, group of 32 W columns), W = 4 waves (up to 128
+// columns per kv head) or 8 (more), wave w owns 32 columns (column c = token
+// * group + head, as there) and walks every key position its columns can
+// see.  The K and V of each 32-key step (two pages) are read from HBM once
+// per unit by all its threads, staged in LDS (double buffered, further steps
+// of loads in flight in registers) and read by the W waves from there.
 //
 // Per step and wave, with v_mfma_f32_32x32x16_bf16:
 //   S^T[32 keys][32 cols]  = K[32][D] . Q^T[D][32]    D/16 products; A = K
@@ -286,11 +286,13 @@ void chunk_lds_kernel(ChunkParams p) {
   for (int db = 0; db < D / 32; ++db) wc.o[db] = f32x16{};
   wc.den = 0.f;
   wc.m_run = -INFINITY;
-  // Keys the wave's first and last real columns see.
+  // Last key the wave's first real column sees: steps wholly at or below it
+  // need no mask.  A wave with no real column (the unit's last columns past
+  // the sequence's) takes the unmasked step too, as far as the context's
+  // keys go: its query is zero, its scores finite, and its output dropped;
+  // masking every step would make it the slowest wave at each barrier.
   const int w_first = c_unit + w * kTile;
-  const int w_last = min(w_first + kTile, cols) - 1;
-  const int pos_lo = w_first < cols ? L - q_len + w_first / G : -1;
-  const int pos_hi = w_first < cols ? L - q_len + w_last / G : -1;
+  const int pos_lo = w_first < cols ? L - q_len + w_first / G : L - 1;
 
   // Steps in flight: step t is computed from LDS buffer t % 2 while step t + 1
   // goes from registers to the other buffer and steps up to t + R - 1 are
