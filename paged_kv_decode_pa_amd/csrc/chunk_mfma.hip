@@ -657,6 +657,15 @@ __global__ __launch_bounds__(kBlock) void cascade_kernel(PrefixParams q, DecodeP
   int seq, kvh, part;
   if (!unit_of(p, b - q.num_units, seq, kvh, part)) return;
   __builtin_amdgcn_s_setprio(3);  // lowered before the page stream starts
+  if (p.grid_partitions == 1 && p.first_partition != nullptr) {
+    // One suffix unit per (sequence, kv head): the longest sequences first,
+    // so the second round of units ends with the short ones.
+    const int slot = (b - q.num_units) / p.num_kv_heads;
+    seq = longest_first(p, slot, threadIdx.x & 63);
+    const int f = p.first_partition[seq];
+    part = f < 0 ? 0 : f > p.num_partitions ? p.num_partitions : f;
+    if (part >= p.num_partitions) return;
+  }
   // Cached loads: the nontemporal hint on these units (a sequence's own
   // partitions, past its group's shared prefix) measured 5% slower.
   whole_unit<D>(p, seq, kvh, part, smem, /*shared=*/true);
