@@ -247,7 +247,7 @@ void chunk_lds_kernel(ChunkParams p) {
   const int kvh = u % p.num_kv_heads;
   const int rest = u / p.num_kv_heads;
   const int grp = rest % p.groups_per_seq;
-  const int seq = longest_first(p, rest / p.groups_per_seq, lane);
+  const int seq = longest_first_of_batch(p, rest / p.groups_per_seq, lane);
   const int G = p.group;
 
   const int q0 = p.query_start[seq];

@@ -311,7 +311,7 @@ void chunk_attention_kernel(ChunkParams p) {
   const int kvh = u % p.num_kv_heads;
   const int rest = u / p.num_kv_heads;
   const int grp = rest % p.groups_per_seq;
-  const int seq = longest_first(p, rest / p.groups_per_seq, lane);
+  const int seq = longest_first_of_batch(p, rest / p.groups_per_seq, lane);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, j = lane >> 4;
   const int G = p.group;
@@ -661,7 +661,7 @@ __global__ __launch_bounds__(kBlock) void cascade_kernel(PrefixParams q, DecodeP
     // One suffix unit per (sequence, kv head): the longest sequences first,
     // so the second round of units ends with the short ones.
     const int slot = (b - q.num_units) / p.num_kv_heads;
-    seq = longest_first(p, slot, threadIdx.x & 63);
+    seq = longest_first_of_batch(p, slot, threadIdx.x & 63);
     const int f = p.first_partition[seq];
     part = f < 0 ? 0 : f > p.num_partitions ? p.num_partitions : f;
     if (part >= p.num_partitions) return;

@@ -274,23 +274,36 @@ __host__ __device__ constexpr int plan_chunks_for(int num_seqs) {
 // instead of a long sequence's units starting late and setting the end.
 // The rank's length is found by a binary search on the count of lengths at
 // or above a threshold (wave ballots), then the tie by its batch order.
-template <class Params>
+// NC: chunks of 64 sequences loaded (NC * 64 >= the batch; the default
+// covers any batch the order applies to).
+template <int NC = kPlanChunks, class Params>
 __device__ inline int longest_first(const Params& p, int rank, int lane) {
-  if (p.num_seqs > kPlanMaxSeqs) return rank;
+  if (p.num_seqs > 64 * NC) return rank;
   const int nc = (p.num_seqs + 63) >> 6;
   const int cap = min(p.max_pages_per_seq, (1 << 30) / kPage - 1) * kPage;
   // The loads go out together, unconditionally (a lane past the batch
   // re-reads the last sequence): under a branch, the compiler waits for each
   // load before the next.
-  int len[kPlanChunks];
+  int len[NC];
 #pragma unroll
-  for (int c = 0; c < kPlanChunks; ++c)
+  for (int c = 0; c < NC; ++c)
     len[c] = p.context_lens[min(64 * c + lane, p.num_seqs - 1)];
 #pragma unroll
-  for (int c = 0; c < kPlanChunks; ++c)
+  for (int c = 0; c < NC; ++c)
     len[c] = 64 * c + lane < p.num_seqs ? min(max(len[c], 0), cap) : -1;  // -1: past the batch
-  const int seq = seq_of_rank<kPlanChunks>(len, nc, rank, lane);
+  const int seq = seq_of_rank<NC>(len, nc, rank, lane);
   return seq >= 0 ? seq : rank;
+}
+
+// longest_first with as many chunks as the batch needs: every wave of a
+// launch runs it, and the chunks past the batch would each re-read one
+// length, the same address from every wave.
+template <class Params>
+__device__ inline int longest_first_of_batch(const Params& p, int rank, int lane) {
+  const int nc = plan_chunks_for(p.num_seqs);
+  if (nc == 1) return longest_first<1>(p, rank, lane);
+  if (nc == 4) return longest_first<4>(p, rank, lane);
+  return longest_first<kPlanChunks>(p, rank, lane);  // batch order past kPlanMaxSeqs
 }
 
 // The sharing test of sequence `seq`: its loads are issued by request(), the
