@@ -53,6 +53,7 @@ CASES = [
     ([1000, 33, 512], [7, 2, 16], 32, 8, 128),           # drafted tokens, group 4
     ([700, 48], [33, 17], 16, 1, 128),                   # group 16: one token per block
     ([257, 90], [40, 90], 8, 8, 64),                     # no grouping: 16 tokens per block
+    ([400, 260], [200, 150], 8, 8, 64),                  # D = 64, eight-wave LDS units
     ([130, 64, 200], [12, 3, 0], 12, 4, 64),             # group 3 straddles blocks; q_len 0
     ([600, 100], [8, 5], 32, 8, 128),                    # two column blocks per wave
     ([2048 + 300], [300], 8, 1, 128),                    # chunked prefill on a long context
