@@ -186,12 +186,15 @@ __device__ inline void wave_step(WaveCols<D>& wc, const char* buf, int t0, bool 
       s[j] = (key > wc.pos || !ok) ? -INFINITY : s[j];
     }
   }
+  // The column's keys are split over lanes l and l ^ 32, whose reference is
+  // the same: some lane's own maximum passes the slack exactly when some
+  // column's does, so the two halves are combined only for a rescale.
   float mx = s[0];
 #pragma unroll
   for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s[j]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float mc = mx * scale_log2;  // -inf stays -inf (scale > 0)
-  if (__ballot(mc > wc.m_run + kLdsSlack) != 0) {
+  const float lc = mx * scale_log2;  // -inf stays -inf (scale > 0)
+  if (__ballot(lc > wc.m_run + kLdsSlack) != 0) {
+    const float mc = fmaxf(lc, __shfl_xor(lc, 32));
     const float m_new = fmaxf(wc.m_run, mc);
     const float alpha = wc.m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(wc.m_run - m_new);
     wc.m_run = m_new;
