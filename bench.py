@@ -51,11 +51,10 @@ CHUNK_LDS_KERNEL_SOURCES = ["paged_kv_decode_pa_amd/csrc/chunk_lds.hip",
                             "paged_kv_decode_pa_amd/csrc/pa_device.hpp"]
 CHUNK_LDS_MIN_COLUMNS = 65  # max_query_len * (q heads per kv head) from which it runs
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
-# --chunk default: split-KV (pa_chunk_attention_split) at this partition size up
-# to this many new tokens per sequence, the single pass above (measured on the
-# Llama-3-8B batch: the split form is faster up to 8 tokens, slower at 16).
-CHUNK_SPLIT_PARTITION = 768
-CHUNK_SPLIT_MAX_Q = 8
+# --chunk default: the single pass (pa_chunk_attention) at every token count
+# (on the Llama-3-8B batch it beats the split form at 768-token partitions from
+# one new token up: 98 against 106 us at 1, 102 against 119 at 4).
+# --chunk-partition PS times pa_chunk_attention_split instead.
 TRANSFER_METRIC = ("KV page hand-off: export every page of the batch to one buffer, import it "
                    "into another pool; GB/s read + written, 1 GPU")
 PAGER_METRIC = ("host page-pool owner: decode steps/s of bookkeeping (one append per "
@@ -115,8 +114,7 @@ def parse_args():
                          "prompts, then decode-step appends and block tables")
     ap.add_argument("--chunk-partition", type=int, default=None, metavar="PS",
                     help="with --chunk: pa_chunk_attention_split at this partition size "
-                         "(0 = the single-pass pa_chunk_attention; default: split at 768 "
-                         "tokens up to 8 new tokens per sequence, single pass above)")
+                         "(default 0 = the single-pass pa_chunk_attention)")
     ap.add_argument("--chunk", type=int, default=0, metavar="Q",
                     help="time pa_chunk_attention with Q new tokens per sequence instead of the "
                          "decode step (the cache write of the Q tokens, then the attention)")
@@ -500,9 +498,7 @@ def run_chunk_config(cid, args):
     lens = torch.from_numpy(wl.context_lens).to(dev)
     out = torch.empty_like(query)
     flush_buf = None if args.no_flush else torch.zeros(1 << 28, dtype=torch.float32, device=dev)
-    cps = args.chunk_partition
-    if cps is None:
-        cps = CHUNK_SPLIT_PARTITION if q <= CHUNK_SPLIT_MAX_Q else 0
+    cps = args.chunk_partition or 0
     if cps:
         n_parts = max(1, -(-int(wl.context_lens.max()) // cps))
         T = B * q

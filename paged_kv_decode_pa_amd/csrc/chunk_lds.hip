@@ -90,7 +90,8 @@ struct StepRegs {
   bool ok0, ok1;  // the step's two page ids are in range
 };
 
-template <int D, int W>
+// NT: the nontemporal hint (pages that no other unit reads).
+template <int D, int W, bool NT>
 __device__ inline void load_step(StepRegs<D, W>& r, const ChunkParams& p, RowIds& ids, int step,
                                  int n_pages, int kvh, int tid, int lane) {
   constexpr int CPP = 2 * D;  // 16-byte chunks per page tile (K or V)
@@ -109,8 +110,15 @@ __device__ inline void load_step(StepRegs<D, W>& r, const ChunkParams& p, RowIds
     const int q = min(tid + UnitShape<D, W>::kThreads * i, 2 * CPP - 1);  // chunk (page q / CPP)
     const size_t base = q < CPP ? b0 : b1;
     const uint32_t off = uint32_t(q % CPP) * 16u;
-    r.k[i] = *reinterpret_cast<const u32x4*>(kp + base + off);
-    r.v[i] = *reinterpret_cast<const u32x4*>(vp + base + off);
+    const u32x4* ka = reinterpret_cast<const u32x4*>(kp + base + off);
+    const u32x4* va = reinterpret_cast<const u32x4*>(vp + base + off);
+    if constexpr (NT) {
+      r.k[i] = __builtin_nontemporal_load(ka);
+      r.v[i] = __builtin_nontemporal_load(va);
+    } else {
+      r.k[i] = *ka;
+      r.v[i] = *va;
+    }
   }
 }
 
@@ -236,11 +244,48 @@ __device__ inline void wave_step(WaveCols<D>& wc, const char* buf, int t0, bool 
     }
 }
 
+// A unit's steps.  Step t is computed from LDS buffer t % 2 while step t + 1
+// goes from registers to the other buffer and steps up to t + R - 1 are
+// loading into the other register sets (set t % R takes step t + R).
+template <int D, int W, bool NT>
+__device__ inline void unit_steps(WaveCols<D>& wc, const ChunkParams& p, RowIds& ids, char* lds,
+                                  int n_steps, int n_pages, int kvh, int L, int pos_lo, int tid,
+                                  int lane) {
+  constexpr int R = UnitShape<D, W>::kRing;
+  char* bufs[2] = {lds, lds + LdsTile<D>::kBuf};
+  // Loads are unconditional (step indices clamped to the last step): with a
+  // load under a branch the compiler cannot count the loads in flight and
+  // waits for all of them before the next use of any loaded register.
+  StepRegs<D, W> r[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    load_step<D, W, NT>(r[i], p, ids, min(i, n_steps - 1), n_pages, kvh, tid, lane);
+  store_step<D, W>(r[0], bufs[0], 0, L, tid);
+  __syncthreads();
+  for (int s = 0; s < n_steps; s += R) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int t = s + i;
+      if (t < n_steps) {  // uniform
+        const bool ok0 = r[i].ok0, ok1 = r[i].ok1;
+        load_step<D, W, NT>(r[i], p, ids, min(t + R, n_steps - 1), n_pages, kvh, tid, lane);
+        const int t0 = kTile * t;
+        const char* buf = (i & 1) ? bufs[1] : bufs[0];
+        // (A wave whose columns see none of the step computes it anyway:
+        // every P is 0, and a skip would again copy the accumulators.)
+        wave_step<D>(wc, buf, t0, !(t0 + kTile - 1 <= pos_lo && ok0 && ok1), ok0, ok1,
+                     p.scale_log2, lane);
+        if (t + 1 < n_steps)
+          store_step<D, W>(r[(i + 1) % R], (i & 1) ? bufs[0] : bufs[1], t0 + kTile, L, tid);
+        __syncthreads();
+      }
+    }
+  }
+}
+
 template <int D, int W>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
 void chunk_lds_kernel(ChunkParams p) {
-  using Shape = UnitShape<D, W>;
-  constexpr int R = Shape::kRing;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int u = blockIdx.x;
   if (u >= p.num_units) return;
@@ -297,39 +342,16 @@ void chunk_lds_kernel(ChunkParams p) {
   const int w_first = c_unit + w * kTile;
   const int pos_lo = w_first < cols ? L - q_len + w_first / G : L - 1;
 
-  // Steps in flight: step t is computed from LDS buffer t % 2 while step t + 1
-  // goes from registers to the other buffer and steps up to t + R - 1 are
-  // loading into the other register sets (set t % R takes step t + R).
-  char* bufs[2] = {lds, lds + LdsTile<D>::kBuf};
+  // A unit whose column group is its sequence's only one, and whose first
+  // page no other sequence starts with, is the only reader of its pages: it
+  // streams them with the nontemporal hint.  (Two instantiations of the step
+  // loop, so that no load sits under a branch.)
+  const bool nt = p.groups_per_seq == 1 && !first_page_shared_of_batch(p, seq, lane);
   if (n_steps > 0) {
-    // Loads are unconditional (step indices clamped to the last step): with
-    // a load under a branch the compiler cannot count the loads in flight and
-    // waits for all of them before the next use of any loaded register.
-    StepRegs<D, W> r[R];
-#pragma unroll
-    for (int i = 0; i < R; ++i)
-      load_step<D, W>(r[i], p, ids, min(i, n_steps - 1), n_pages, kvh, tid, lane);
-    store_step<D, W>(r[0], bufs[0], 0, L, tid);
-    __syncthreads();
-    for (int s = 0; s < n_steps; s += R) {
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        const int t = s + i;
-        if (t < n_steps) {  // uniform
-          const bool ok0 = r[i].ok0, ok1 = r[i].ok1;
-          load_step<D, W>(r[i], p, ids, min(t + R, n_steps - 1), n_pages, kvh, tid, lane);
-          const int t0 = kTile * t;
-          const char* buf = (i & 1) ? bufs[1] : bufs[0];
-          // (A wave whose columns see none of the step computes it anyway:
-          // every P is 0, and a skip would again copy the accumulators.)
-          wave_step<D>(wc, buf, t0, !(t0 + kTile - 1 <= pos_lo && ok0 && ok1), ok0, ok1,
-                       p.scale_log2, lane);
-          if (t + 1 < n_steps)
-            store_step<D, W>(r[(i + 1) % R], (i & 1) ? bufs[0] : bufs[1], t0 + kTile, L, tid);
-          __syncthreads();
-        }
-      }
-    }
+    if (nt)
+      unit_steps<D, W, true>(wc, p, ids, lds, n_steps, n_pages, kvh, L, pos_lo, tid, lane);
+    else
+      unit_steps<D, W, false>(wc, p, ids, lds, n_steps, n_pages, kvh, L, pos_lo, tid, lane);
   }
 
   // out = O / den for the wave's real columns.  Lane l holds column l % 32,

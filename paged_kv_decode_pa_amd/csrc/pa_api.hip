@@ -319,6 +319,12 @@ int chunk_impl(void* out, const void* query, const void* k_cache, const void* v_
   p.partial_max = partial_max;
   p.partial_sum = partial_sum;
   p.first_partition = nullptr;
+  p.snake_period = 0;
+  if (!split && !lds) {
+    const int cus = device_compute_units();
+    const int64_t per_round = int64_t(num_kv_heads) * groups;
+    p.snake_period = cus > 0 ? int(cus / per_round > 0 ? cus / per_round : 1) : 0;
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   if ((lds ? pa::launch_chunk_lds(p, head_dim, lds_waves, st)
            : pa::launch_chunk_attention(p, head_dim, st)) !=

@@ -119,6 +119,7 @@ struct ChunkParams {
   float* partial_max;
   float* partial_sum;
   const int32_t* first_partition;  // always NULL here (the unit plan's field)
+  int snake_period;                 // single pass: compute units per round of units (0: none)
 };
 
 // Number of workgroups: one per work unit.

@@ -306,6 +306,26 @@ __device__ inline int longest_first_of_batch(const Params& p, int rank, int lane
   return longest_first<kPlanChunks>(p, rank, lane);  // batch order past kPlanMaxSeqs
 }
 
+// Whether sequence `seq`'s first page is another sequence's too, for a
+// kernel not specialised on the batch size (true past the batch sizes the
+// plan covers: those take cached loads).
+template <class Params>
+__device__ inline bool first_page_shared_of_batch(const Params& p, int seq, int lane) {
+  bool shared = true;
+  switch (plan_chunks_for(p.num_seqs)) {
+    case 1: { FirstPages<1> fp; fp.request(p, lane); shared = fp.shared(p, seq, lane); break; }
+    case 4: { FirstPages<4> fp; fp.request(p, lane); shared = fp.shared(p, seq, lane); break; }
+    case kPlanChunks: {
+      FirstPages<kPlanChunks> fp;
+      fp.request(p, lane);
+      shared = fp.shared(p, seq, lane);
+      break;
+    }
+    default: break;
+  }
+  return __builtin_amdgcn_readfirstlane(int(shared)) != 0;
+}
+
 // The sharing test of sequence `seq`: its loads are issued by request(), the
 // answer is read by shared() after other loads have been issued.
 template <int NC>

@@ -117,7 +117,7 @@ def test_many_sequences_with_equal_lengths(B):
 @pytest.mark.parametrize("q", [16, 64])
 def test_bench_shape_on_sampled_sequences(q):
     """q new tokens for each of config 2's 64 sequences, the single-pass launch
-    that the multi-token bench times at q > 8.  The GPU runs the whole batch;
+    that the multi-token bench times.  The GPU runs the whole batch;
     the oracle checks eight sequences (the longest, the shortest and six
     seeded picks), every row of each."""
     say(f"[chunk] config 2 shape, {q} new tokens per sequence, sampled oracle")

@@ -189,7 +189,7 @@ def exact_chunk(mode, q_len):
 
 
 @pytest.mark.parametrize("mode", ["flat", "comb"])
-@pytest.mark.parametrize("q_len", [4, 16])
+@pytest.mark.parametrize("q_len", [1, 4, 8, 16])
 def test_chunk_attention_exact(mode, q_len):
     say(f"[exact] pa_chunk_attention config 2 lengths, {q_len} new tokens, {mode}")
     query, qs, want = exact_chunk(mode, q_len)
