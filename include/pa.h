@@ -206,10 +206,10 @@ int pa_chunk_attention(void* out, const void* query, const void* k_cache, const 
 
 /*
  * pa_chunk_attention_split — pa_chunk_attention as split-KV work units and
- * their log-sum-exp merge, in one call: for a few new tokens per sequence
- * (draft verification), where the single-pass units take as long as the
- * longest sequence.  The same contraction as pa_chunk_attention; the
- * partitions and their merge are those of pa_decode (split) and
+ * their log-sum-exp merge, in one call, for callers that want the split
+ * decode's partial layout per new token (or, through the _noalloc form
+ * below, no caller workspace).  The same contraction as pa_chunk_attention;
+ * the partitions and their merge are those of pa_decode (split) and
  * pa_decode_reduce, per new token.
  *
  *   partition_size      tokens per partition, a positive multiple of 16.

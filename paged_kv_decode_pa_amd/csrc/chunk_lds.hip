@@ -343,10 +343,13 @@ void chunk_lds_kernel(ChunkParams p) {
   const int pos_lo = w_first < cols ? L - q_len + w_first / G : L - 1;
 
   // A unit whose column group is its sequence's only one, and whose first
-  // page no other sequence starts with, is the only reader of its pages: it
-  // streams them with the nontemporal hint.  (Two instantiations of the step
-  // loop, so that no load sits under a branch.)
-  const bool nt = p.groups_per_seq == 1 && !first_page_shared_of_batch(p, seq, lane);
+  // page no other sequence starts with, is the only reader of its pages: a
+  // four-wave unit (two per compute unit) streams them with the nontemporal
+  // hint.  (Eight-wave units measured no faster with it, and fetched 2.6%
+  // more.)  Two instantiations of the step loop, so that no load sits under
+  // a branch.
+  const bool nt =
+      W == 4 && p.groups_per_seq == 1 && !first_page_shared_of_batch(p, seq, lane);
   if (n_steps > 0) {
     if (nt)
       unit_steps<D, W, true>(wc, p, ids, lds, n_steps, n_pages, kvh, L, pos_lo, tid, lane);
