@@ -295,7 +295,14 @@ void chunk_lds_kernel(ChunkParams p) {
   const int kvh = u % p.num_kv_heads;
   const int rest = u / p.num_kv_heads;
   const int grp = rest % p.groups_per_seq;
-  const int seq = longest_first_of_batch(p, rest / p.groups_per_seq, lane);
+  // Four-wave units run two per compute unit, all resident at once: the
+  // single-pass decode's snake order by length balances each compute unit's
+  // pair.  Eight-wave units run one per compute unit in rounds, where
+  // longest first lets the dispatcher even them out.
+  bool shared = true;
+  const int seq = W == 4 && p.snake_period > 0
+                      ? snake_unit_seq_of_batch(p, rest / p.groups_per_seq, lane, shared)
+                      : longest_first_of_batch(p, rest / p.groups_per_seq, lane);
   const int G = p.group;
 
   const int q0 = p.query_start[seq];
@@ -348,8 +355,7 @@ void chunk_lds_kernel(ChunkParams p) {
   // hint.  (Eight-wave units measured no faster with it, and fetched 2.6%
   // more.)  Two instantiations of the step loop, so that no load sits under
   // a branch.
-  const bool nt =
-      W == 4 && p.groups_per_seq == 1 && !first_page_shared_of_batch(p, seq, lane);
+  const bool nt = W == 4 && p.groups_per_seq == 1 && !shared;
   if (n_steps > 0) {
     if (nt)
       unit_steps<D, W, true>(wc, p, ids, lds, n_steps, n_pages, kvh, L, pos_lo, tid, lane);

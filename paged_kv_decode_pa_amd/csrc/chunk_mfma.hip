@@ -305,29 +305,6 @@ __host__ __device__ inline size_t chunk_query_lds_bytes(int head_dim, int nb) {
   return chunk_query_in_lds(nb) ? size_t(nb) * (head_dim / 32) * 64 * 16 : 0;
 }
 
-// The single-pass unit's sequence, as the single-pass decode picks it: slot
-// i takes the sequence of rank snake_rank(i) by length, longest first (batch
-// order when neighbours share their first page), and `shared` says whether
-// its first page is another sequence's too (else it streams with the
-// nontemporal hint).
-template <int NC>
-__device__ inline int chunk_unit_seq(const ChunkParams& p, int slot, int lane, bool& shared) {
-  FirstPages<NC> fp;
-  fp.request(p, lane);
-  const int cap = min(p.max_pages_per_seq, (1 << 30) / kPage - 1) * kPage;
-  int len[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c)
-    len[c] = 64 * c + lane < p.num_seqs ? min(max(fp.len[c], 0), cap) : -1;
-  int seq = slot;
-  if (!fp.adjacent_shared(p, lane)) {
-    const int s = seq_of_rank<NC>(len, NC, snake_rank(slot, p.snake_period, p.num_seqs), lane);
-    seq = s >= 0 ? s : slot;
-  }
-  shared = fp.shared(p, seq, lane);
-  return seq;
-}
-
 template <int D, int NB>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(NB >= 3 ? 2 : 1)))
 void chunk_attention_kernel(ChunkParams p) {
@@ -339,16 +316,9 @@ void chunk_attention_kernel(ChunkParams p) {
   const int rest = u / p.num_kv_heads;
   const int grp = rest % p.groups_per_seq;
   const int slot = rest / p.groups_per_seq;
-  bool shared = true;
-  int seq = slot;
-  switch (plan_chunks_for(p.num_seqs)) {
-    case 1: seq = chunk_unit_seq<1>(p, slot, lane, shared); break;
-    case 4: seq = chunk_unit_seq<4>(p, slot, lane, shared); break;
-    case kPlanChunks: seq = chunk_unit_seq<kPlanChunks>(p, slot, lane, shared); break;
-    default: break;
-  }
-  seq = __builtin_amdgcn_readfirstlane(seq);
-  shared = __builtin_amdgcn_readfirstlane(int(shared)) != 0 || p.groups_per_seq > 1;
+  bool shared;
+  const int seq = snake_unit_seq_of_batch(p, slot, lane, shared);
+  shared = shared || p.groups_per_seq > 1;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, j = lane >> 4;
   const int G = p.group;

@@ -319,8 +319,10 @@ int chunk_impl(void* out, const void* query, const void* k_cache, const void* v_
   p.partial_max = partial_max;
   p.partial_sum = partial_sum;
   p.first_partition = nullptr;
+  // Single pass: units per round over the compute units, for the snake
+  // order (the register kernel and four-wave LDS units).
   p.snake_period = 0;
-  if (!split && !lds) {
+  if (!split && (!lds || lds_waves == 4)) {
     const int cus = device_compute_units();
     const int64_t per_round = int64_t(num_kv_heads) * groups;
     p.snake_period = cus > 0 ? int(cus / per_round > 0 ? cus / per_round : 1) : 0;

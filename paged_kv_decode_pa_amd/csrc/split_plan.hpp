@@ -306,24 +306,43 @@ __device__ inline int longest_first_of_batch(const Params& p, int rank, int lane
   return longest_first<kPlanChunks>(p, rank, lane);  // batch order past kPlanMaxSeqs
 }
 
-// Whether sequence `seq`'s first page is another sequence's too, for a
-// kernel not specialised on the batch size (true past the batch sizes the
-// plan covers: those take cached loads).
+// The sequence of a single-pass unit in slot `slot` when all the launch's
+// units are resident at once, as the single-pass decode picks it: the
+// sequence of rank snake_rank(slot) by length, longest first (batch order
+// when neighbours share their first page), so that each compute unit's
+// units add up to about the same work.  `shared` says whether its first page
+// is another sequence's too (else it may stream with the nontemporal hint).
+// Past the batch sizes the plan covers: batch order, shared.
+template <int NC, class Params>
+__device__ inline int snake_unit_seq(const Params& p, int slot, int lane, bool& shared) {
+  FirstPages<NC> fp;
+  fp.request(p, lane);
+  const int cap = min(p.max_pages_per_seq, (1 << 30) / kPage - 1) * kPage;
+  int len[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    len[c] = 64 * c + lane < p.num_seqs ? min(max(fp.len[c], 0), cap) : -1;
+  int seq = slot;
+  if (!fp.adjacent_shared(p, lane)) {
+    const int s = seq_of_rank<NC>(len, NC, snake_rank(slot, p.snake_period, p.num_seqs), lane);
+    seq = s >= 0 ? s : slot;
+  }
+  shared = fp.shared(p, seq, lane);
+  return seq;
+}
+
 template <class Params>
-__device__ inline bool first_page_shared_of_batch(const Params& p, int seq, int lane) {
-  bool shared = true;
+__device__ inline int snake_unit_seq_of_batch(const Params& p, int slot, int lane, bool& shared) {
+  int seq = slot;
+  shared = true;
   switch (plan_chunks_for(p.num_seqs)) {
-    case 1: { FirstPages<1> fp; fp.request(p, lane); shared = fp.shared(p, seq, lane); break; }
-    case 4: { FirstPages<4> fp; fp.request(p, lane); shared = fp.shared(p, seq, lane); break; }
-    case kPlanChunks: {
-      FirstPages<kPlanChunks> fp;
-      fp.request(p, lane);
-      shared = fp.shared(p, seq, lane);
-      break;
-    }
+    case 1: seq = snake_unit_seq<1>(p, slot, lane, shared); break;
+    case 4: seq = snake_unit_seq<4>(p, slot, lane, shared); break;
+    case kPlanChunks: seq = snake_unit_seq<kPlanChunks>(p, slot, lane, shared); break;
     default: break;
   }
-  return __builtin_amdgcn_readfirstlane(int(shared)) != 0;
+  shared = __builtin_amdgcn_readfirstlane(int(shared)) != 0;
+  return __builtin_amdgcn_readfirstlane(seq);
 }
 
 // The sharing test of sequence `seq`: its loads are issued by request(), the
