@@ -114,6 +114,22 @@ def test_many_sequences_with_equal_lengths(B):
     assert np.array_equal(bits_of(run_chunk(dev, query, qs)), bits_of(got))
 
 
+def test_lds_units_past_the_ordered_batch_sizes():
+    """1100 sequences with 17-20 new tokens at a group of 4 (68-80 columns:
+    four-wave LDS units), past the batch sizes whose units are ordered by
+    length (they run in batch order); every row against the oracle."""
+    say("[chunk] 1100 sequences, LDS units in batch order")
+    rng = np.random.default_rng(1700)
+    lens = rng.choice([20, 33, 40, 97], size=1100).tolist()
+    wl = make_custom_workload(lens, num_q_heads=8, num_kv_heads=2, head_dim=64, seed=1701)
+    q_lens = [min(n, int(rng.integers(17, 21))) for n in lens]
+    query, qs = make_chunk_queries(wl, q_lens, seed=1702)
+    ref = chunk_reference(wl, query, qs)
+    got = run_chunk(DeviceWorkload(wl), query, qs)
+    assert max(q_lens) * 4 > LDS_MIN_COLUMNS
+    assert max_err(got, ref) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("q", [16, 64])
 def test_bench_shape_on_sampled_sequences(q):
     """q new tokens for each of config 2's 64 sequences, the single-pass launch
@@ -129,6 +145,30 @@ def test_bench_shape_on_sampled_sequences(q):
     rng = np.random.default_rng(q)
     pick = sorted({int(lens.argmax()), int(lens.argmin()),
                    *rng.choice(wl.num_seqs, 6, replace=False).tolist()})
+    k, v = fill_pools(oracle, wl)
+    for b in pick:
+        lo, hi = int(qs[b]), int(qs[b + 1])
+        ref = oracle.chunk_attention(query[lo:hi], k, v, wl.block_tables[b:b + 1],
+                                     wl.context_lens[b:b + 1], np.array([0, hi - lo]),
+                                     wl.scale, wl.page_size, wl.dtype)
+        err = float(np.abs(got[lo:hi] - ref).max())
+        assert err <= TOL["bf16"], (b, err)
+
+
+@pytest.mark.parametrize("q", [4, 32])
+def test_prefix_groups_on_sampled_sequences(q):
+    """q new tokens for each of the prefix-reuse batch's 128 sequences (8
+    groups of 16 sharing their first 128 pages): neighbours share a first
+    page, so the single-pass units keep batch order and cached loads (the
+    register kernel at q = 4, four-wave LDS units at q = 32).  Eight sampled
+    sequences against the oracle, every row of each."""
+    say(f"[chunk] prefix-reuse batch, {q} new tokens per sequence, sampled oracle")
+    wl = config_workload(3)
+    query, qs = make_chunk_queries(wl, [q] * wl.num_seqs, seed=300 + q)
+    got = run_chunk(config_device(3), query, qs).float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(q)
+    pick = sorted({0, 15, 16, wl.num_seqs - 1, *rng.choice(wl.num_seqs, 4, replace=False).tolist()})
     k, v = fill_pools(oracle, wl)
     for b in pick:
         lo, hi = int(qs[b]), int(qs[b + 1])
