@@ -124,23 +124,8 @@ __global__ __launch_bounds__(kBlock) void decode_whole_kernel(DecodeParams p) {
   if (!unit_of(p, blockIdx.x, seq, kvh, part)) return;
   __builtin_amdgcn_s_setprio(3);  // lowered before the page stream starts
   bool shared = true;
-  if constexpr (NC > 0) {
-    if (p.pages_per_partition == 0) {
-      const int lane = threadIdx.x & 63;
-      FirstPages<NC> fp;
-      fp.request(p, lane);
-      const int cap = min(p.max_pages_per_seq, (1 << 30) / kPage - 1) * kPage;
-      int len[NC];
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-        len[c] = 64 * c + lane < p.num_seqs ? min(max(fp.len[c], 0), cap) : -1;
-      if (!fp.adjacent_shared(p, lane)) {
-        const int s = seq_of_rank<NC>(len, NC, snake_rank(seq, p.snake_period, p.num_seqs), lane);
-        seq = s >= 0 ? s : seq;
-      }
-      shared = fp.shared(p, seq, lane);
-    }
-  }
+  if constexpr (NC > 0)
+    if (p.pages_per_partition == 0) seq = snake_unit_seq<NC>(p, seq, threadIdx.x & 63, shared);
   whole_unit<D>(p, seq, kvh, part, smem, shared);
 }
 
