@@ -62,7 +62,8 @@ def test_one_token_per_sequence_is_split_decode(cid, ps):
                                   (8, 768)])
 def test_draft_verification_at_config_2_shape(q, ps):
     """q new tokens for each of config 2's 64 sequences; 768-token partitions
-    are the split form's default at this shape (q <= 8)."""
+    are the split form's benchmarked size at this shape
+    (bench.py --chunk Q --chunk-partition 768)."""
     say(f"[chunk split] config 2 shape, {q} new tokens per sequence, partition {ps}")
     wl = config_workload(2)
     query, qs = make_chunk_queries(wl, [q] * wl.num_seqs, seed=q)
