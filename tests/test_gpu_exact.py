@@ -197,17 +197,20 @@ def test_chunk_attention_exact(mode, q_len):
 
 
 @pytest.mark.parametrize("mode", ["flat", "comb"])
-def test_chunk_attention_lds_exact(mode):
-    """64 new tokens per sequence (256 columns per kv head at group 4: the
-    kernel that stages K/V in LDS), on the eight longest of config 2's
-    lengths (the oracle of all 64 sequences takes about a minute)."""
-    say(f"[exact] pa_chunk_attention, 64 new tokens, eight longest config 2 lengths, {mode}")
+@pytest.mark.parametrize("q_len", [32, 64])
+def test_chunk_attention_lds_exact(mode, q_len):
+    """32 or 64 new tokens per sequence (128 or 256 columns per kv head at
+    group 4: the kernel that stages K/V in LDS, in four-wave units in the
+    snake order with nontemporal loads, or eight-wave units longest first),
+    on the eight longest of config 2's lengths (the oracle of all 64
+    sequences takes about a minute)."""
+    say(f"[exact] pa_chunk_attention, {q_len} new tokens, eight longest config 2 lengths, {mode}")
     cfg = config_by_id(2)
     lens = sorted(config_workload(2).context_lens.tolist(), reverse=True)[:8]
     wl = make_custom_workload(lens, num_q_heads=cfg.num_q_heads, num_kv_heads=cfg.num_kv_heads,
                               head_dim=cfg.head_dim, dtype=cfg.dtype, seed=640,
                               value_fn=indicator_values(mode))
-    query, qs = make_chunk_queries(wl, [64] * wl.num_seqs, seed=64,
+    query, qs = make_chunk_queries(wl, [q_len] * wl.num_seqs, seed=q_len,
                                    value_fn=chunk_query_values(mode))
     want = oracle.round_to_bf16_bits(chunk_reference(wl, query, qs))
     check_exact(run_chunk(DeviceWorkload(wl), query, qs), want, "pa_chunk_attention (LDS)")
