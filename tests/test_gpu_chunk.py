@@ -179,6 +179,39 @@ def test_prefix_groups_on_sampled_sequences(q):
         assert err <= TOL["bf16"], (b, err)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_chunk_random(seed):
+    """Seeded random batches through both single-pass kernels: kv heads, group
+    size, head dim, batch size (some contexts empty or one token long), new
+    tokens per sequence up to 40 (so that max_query_len * group runs from a
+    few columns to hundreds, across the register and LDS kernels), optional
+    prefix groups (batch order, cached loads).  Every row against the oracle."""
+    rng = np.random.default_rng(5000 + seed)
+    B = int(rng.integers(1, 48))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    D = int(rng.choice([64, 128]))
+    lens = np.where(rng.random(B) < 0.15, rng.integers(0, 2, B), rng.integers(2, 700, B))
+    kw = {}
+    if B >= 4 and rng.random() < 0.4:
+        n_groups = int(rng.integers(1, 3))
+        group_of = np.where(np.arange(B) < 2 * n_groups * 2, np.arange(B) // 4 % n_groups, -1)
+        group_of = np.where(np.arange(B) < 4 * n_groups, group_of, -1)
+        prefix = 16 * int(rng.integers(1, 8))
+        lens = np.where(group_of >= 0, prefix + rng.integers(1, 100, B), lens)
+        kw = dict(group_of=group_of.tolist(), prefix_tokens=prefix)
+    q_cap = int(rng.choice([4, 16, 40]))
+    q_lens = [int(min(n, rng.integers(1, q_cap + 1))) for n in lens]
+    say(f"[chunk random {seed}] B={B} {Hkv * G}/{Hkv}/{D} q up to {max(q_lens)} "
+        f"({max(q_lens) * G} columns) groups {bool(kw)}")
+    wl = make_custom_workload([int(x) for x in lens], num_q_heads=Hkv * G, num_kv_heads=Hkv,
+                              head_dim=D, seed=seed, placement_seed=seed + 7, **kw)
+    query, qs = make_chunk_queries(wl, q_lens, seed=seed + 11)
+    ref = chunk_reference(wl, query, qs)
+    got = run_chunk(DeviceWorkload(wl), query, qs)
+    assert max_err(got, ref) <= TOL["bf16"]
+
+
 def test_later_tokens_never_reach_earlier_rows():
     say("[chunk] causality on the GPU")
     wl = make_custom_workload([200], num_q_heads=8, num_kv_heads=2, head_dim=128, seed=5)
