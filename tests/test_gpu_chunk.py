@@ -130,7 +130,7 @@ def test_lds_units_past_the_ordered_batch_sizes():
     assert max_err(got, ref) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("q", [16, 32, 64])
+@pytest.mark.parametrize("q", [16, 32, 64, 128])
 def test_bench_shape_on_sampled_sequences(q):
     """q new tokens for each of config 2's 64 sequences, the single-pass launch
     that the multi-token bench times.  The GPU runs the whole batch;
