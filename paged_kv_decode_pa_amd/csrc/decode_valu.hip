@@ -1,14 +1,15 @@
 // Paged decode on the vector ALU: fp32 and bf16, head_dim 64/128, groups up
-// to 16.  Same work units, page walk and merge as the matrix-core kernel;
-// only the per-page arithmetic differs.
+// to 16.  Same work units and merge as the matrix-core kernel (four waves per
+// unit, wave w taking every fourth page); each wave keeps two pages in flight.
 //
 // Per page and kv head, lane (t, c) = (lane / 4, lane % 4) holds token t's
 // key slice [c*D/4, (c+1)*D/4) and forms partial dots against the query
-// group (kept in LDS as fp32); two xor-shuffles finish each score.  The page
-// maximum per head is a four-step xor-shuffle over the tokens.  For P.V, lane
-// d owns output dims d and d+64 and reads those dims' 16 value slots (the V
-// page is stored dim-major, so that is one contiguous row per dim); each
-// token's weight is broadcast from its owner lane with readlane.
+// group (kept in LDS as fp32); a quad butterfly (DPP) finishes each score.
+// The page maximum per head comes from DPP mirrors and gfx950's lane-swap
+// instructions, without an LDS round trip.  For P.V, lane d owns output dims
+// d and d+64 and reads those dims' 16 value slots (the V page is stored
+// dim-major, so that is one contiguous row per dim); each token's weight is
+// broadcast from its owner lane with readlane.
 #include "pa_device.hpp"
 
 namespace pa {
@@ -16,46 +17,71 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <typename T> struct Load;
-template <> struct Load<float> {
-  // n floats (n % 4 == 0) from 16-byte aligned global memory
-  template <int n> __device__ static void run(const void* src, float* dst) {
-    const u32x4* s = static_cast<const u32x4*>(src);
-#pragma unroll
-    for (int i = 0; i < n / 4; ++i) {
-      const u32x4 v = s[i];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dst[4 * i + e] = __uint_as_float(v[e]);
-    }
-  }
-};
-template <> struct Load<uint16_t> {
-  // n bf16 values (n % 8 == 0), widened exactly
-  template <int n> __device__ static void run(const void* src, float* dst) {
-    const u32x4* s = static_cast<const u32x4*>(src);
-#pragma unroll
-    for (int i = 0; i < n / 8; ++i) {
-      const u32x4 v = s[i];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        dst[8 * i + 2 * e] = __uint_as_float(v[e] << 16);
-        dst[8 * i + 2 * e + 1] = __uint_as_float(v[e] & 0xffff0000u);
-      }
-    }
-  }
-};
-
 template <typename T>
 __device__ inline float load_one(const void* base, size_t i) {
   if constexpr (sizeof(T) == 4) return static_cast<const float*>(base)[i];
   else return bf16_to_f32(static_cast<const uint16_t*>(base)[i]);
 }
 
+// One page's K slice and V rows of a lane, as loaded (bf16 or fp32 bits).
 template <typename T, int D>
+struct RawPage {
+  static constexpr int KQ = D / 4 * sizeof(T) / 16;      // 16-byte loads of the key slice
+  static constexpr int VQ = kPage * sizeof(T) / 16;      // 16-byte loads per value row
+  u32x4 k[KQ];
+  u32x4 v[D / 64][VQ];
+};
+
+template <typename T, int n>
+__device__ inline void widen(const u32x4* src, float* dst) {
+  if constexpr (sizeof(T) == 4) {
+#pragma unroll
+    for (int i = 0; i < n / 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[4 * i + e] = __uint_as_float(src[i][e]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < n / 8; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dst[8 * i + 2 * e] = __uint_as_float(src[i][e] << 16);
+        dst[8 * i + 2 * e + 1] = __uint_as_float(src[i][e] & 0xffff0000u);
+      }
+  }
+}
+
+// The sum over a lane quad (a token's four key slices), in the order of two
+// xor-butterflies: lanes 1,0,3,2 then 2,3,0,1 of each quad (DPP).
+__device__ inline float quad_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+  return x;
+}
+
+// The maximum over the wave's 16 tokens of a value that is equal within each
+// quad: mirrors inside 8 and 16 lanes (DPP), then the row and half swaps of
+// gfx950 (v_permlane16_swap, v_permlane32_swap).  No LDS round trip.
+__device__ inline float token_max(float m) {
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x141, 0xF, 0xF,
+                                                          false)));  // row_half_mirror
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x140, 0xF, 0xF,
+                                                          false)));  // row_mirror
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false,
+                                                  false);
+  m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false,
+                                                  false);
+  return fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+}
+
+// GB: a bound on the group (1, 2, 4, 8 or 16), so that the per-head state
+// is indexed by unrolled constants only.
+template <typename T, int D, int GB>
 __global__ __launch_bounds__(kBlock) void decode_valu_kernel(DecodeParams p) {
   extern __shared__ float smem[];
   constexpr int QD = D / 4;    // key dims per lane
   constexpr int VD = D / 64;   // value dims per lane
+  typedef RawPage<T, D> Raw;
   int seq, kvh, part;
   if (!unit_of(p, blockIdx.x, seq, kvh, part)) return;
   const int L = p.context_lens[seq];
@@ -81,28 +107,47 @@ __global__ __launch_bounds__(kBlock) void decode_valu_kernel(DecodeParams p) {
   const int c = lane & 3;
   const int32_t* table = p.block_tables + size_t(seq) * p.max_pages_per_seq;
   const size_t tile_elems = size_t(kPage) * D;
+  const int n_my = w < hi - lo ? (hi - lo - w + kWaves - 1) / kWaves : 0;  // this wave's pages
 
-  float m_run[kMaxGroup], l_run[kMaxGroup], acc[kMaxGroup][VD];
+  float m_run[GB], l_run[GB], acc[GB][VD];
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) {
+  for (int h = 0; h < GB; ++h) {
     m_run[h] = -INFINITY;
     l_run[h] = 0.f;
 #pragma unroll
     for (int i = 0; i < VD; ++i) acc[h][i] = 0.f;
   }
 
-  for (int i = lo + w; i < hi; i += kWaves) {
-    const int page = table[i];
-    if (page < 0 || page >= p.num_pages) continue;
-    const size_t base = (size_t(page) * p.num_kv_heads + kvh) * tile_elems;
-    const int valid = L - i * kPage;
+  // The wave's k-th page (clamped to its last): loads issued unconditionally,
+  // so that the compiler counts the loads in flight exactly; an out-of-range
+  // id loads page 0 and the page is skipped.
+  auto issue = [&](Raw& r, int k, int& ord, bool& ok) {
+    const int kk = min(k, n_my - 1);
+    ord = lo + w + kk * kWaves;
+    const int page = table[ord];
+    ok = k < n_my && page >= 0 && page < p.num_pages;
+    const size_t base = (size_t(ok ? page : 0) * p.num_kv_heads + kvh) * tile_elems;
+    const u32x4* ks = reinterpret_cast<const u32x4*>(static_cast<const T*>(p.k_cache) + base +
+                                                     t * D + c * QD);
+#pragma unroll
+    for (int i = 0; i < Raw::KQ; ++i) r.k[i] = ks[i];
+#pragma unroll
+    for (int vi = 0; vi < VD; ++vi) {
+      const u32x4* vs = reinterpret_cast<const u32x4*>(static_cast<const T*>(p.v_cache) + base +
+                                                       (lane + 64 * vi) * kPage);
+#pragma unroll
+      for (int i = 0; i < Raw::VQ; ++i) r.v[vi][i] = vs[i];
+    }
+  };
+
+  auto compute = [&](const Raw& r, int ord) {
+    const int valid = L - ord * kPage;
     float kv[QD];
-    Load<T>::template run<QD>(static_cast<const T*>(p.k_cache) + base + t * D + c * QD, kv);
+    widen<T, QD>(r.k, kv);
     float vv[VD][kPage];
 #pragma unroll
     for (int vi = 0; vi < VD; ++vi) {
-      Load<T>::template run<kPage>(static_cast<const T*>(p.v_cache) + base + (lane + 64 * vi) * kPage,
-                                   vv[vi]);
+      widen<T, kPage>(r.v[vi], vv[vi]);
       if (valid < kPage) {
 #pragma unroll
         for (int tt = 0; tt < kPage; ++tt)
@@ -110,50 +155,74 @@ __global__ __launch_bounds__(kBlock) void decode_valu_kernel(DecodeParams p) {
       }
     }
 #pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) {
-      if (h >= G) break;
-      const float* qh = qs + h * D + c * QD;
-      float part_dot = 0.f;
+    for (int h = 0; h < GB; ++h) {
+      if (h < G) {  // uniform
+        const float* qh = qs + h * D + c * QD;
+        float part_dot = 0.f;
 #pragma unroll
-      for (int e = 0; e < QD; ++e) part_dot = fmaf(qh[e], kv[e], part_dot);
-      part_dot += __shfl_xor(part_dot, 1);
-      part_dot += __shfl_xor(part_dot, 2);
-      const float s2 = (t < valid) ? part_dot * p.scale_log2 : -INFINITY;
-      float pm = s2;
-      pm = fmaxf(pm, __shfl_xor(pm, 4));
-      pm = fmaxf(pm, __shfl_xor(pm, 8));
-      pm = fmaxf(pm, __shfl_xor(pm, 16));
-      pm = fmaxf(pm, __shfl_xor(pm, 32));
-      const float m_new = fmaxf(m_run[h], pm);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[h] - m_new);
-      m_run[h] = m_new;
-      const float pe = __builtin_amdgcn_exp2f(s2 - m_new);
-      l_run[h] = l_run[h] * alpha + (c == 0 ? pe : 0.f);
+        for (int e = 0; e < QD; ++e) part_dot = fmaf(qh[e], kv[e], part_dot);
+        const float s2 = (t < valid) ? quad_sum(part_dot) * p.scale_log2 : -INFINITY;
+        const float m_new = fmaxf(m_run[h], token_max(s2));
+        const float alpha = __builtin_amdgcn_exp2f(m_run[h] - m_new);
+        m_run[h] = m_new;
+        const float pe = __builtin_amdgcn_exp2f(s2 - m_new);
+        l_run[h] = l_run[h] * alpha + (c == 0 ? pe : 0.f);
 #pragma unroll
-      for (int vi = 0; vi < VD; ++vi) acc[h][vi] *= alpha;
+        for (int vi = 0; vi < VD; ++vi) acc[h][vi] *= alpha;
 #pragma unroll
-      for (int tt = 0; tt < kPage; ++tt) {
-        const float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pe), 4 * tt));
+        for (int tt = 0; tt < kPage; ++tt) {
+          const float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pe), 4 * tt));
 #pragma unroll
-        for (int vi = 0; vi < VD; ++vi) acc[h][vi] = fmaf(wt, vv[vi][tt], acc[h][vi]);
+          for (int vi = 0; vi < VD; ++vi) acc[h][vi] = fmaf(wt, vv[vi][tt], acc[h][vi]);
+        }
       }
+    }
+  };
+
+  // Two pages in flight: page k + 1 loads while page k is computed.
+  if (n_my > 0) {
+    Raw r0, r1;
+    int o0, o1;
+    bool ok0, ok1;
+    issue(r0, 0, o0, ok0);
+    for (int k = 0; k < n_my; k += 2) {
+      issue(r1, k + 1, o1, ok1);
+      if (ok0) compute(r0, o0);
+      issue(r0, k + 2, o0, ok0);
+      if (ok1) compute(r1, o1);
     }
   }
 
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) {
-    if (h >= G) break;
-    float l = l_run[h];
+  for (int h = 0; h < GB; ++h) {
+    if (h < G) {
+      float l = l_run[h];
 #pragma unroll
-    for (int x = 1; x < 64; x <<= 1) l += __shfl_xor(l, x);
-    if (lane == 0) {
-      lds.m[w * kMaxGroup + h] = m_run[h];
-      lds.l[w * kMaxGroup + h] = l;
+      for (int x = 1; x < 64; x <<= 1) l += __shfl_xor(l, x);
+      if (lane == 0) {
+        lds.m[w * kMaxGroup + h] = m_run[h];
+        lds.l[w * kMaxGroup + h] = l;
+      }
+#pragma unroll
+      for (int vi = 0; vi < VD; ++vi)
+        lds.acc[(w * G + h) * (D + kAccPad) + lane + 64 * vi] = acc[h][vi];
     }
-#pragma unroll
-    for (int vi = 0; vi < VD; ++vi) lds.acc[(w * G + h) * (D + kAccPad) + lane + 64 * vi] = acc[h][vi];
   }
   merge_and_store<T, D>(p, lds, seq, kvh, part);
+}
+
+template <typename T, int D>
+void launch_g(const DecodeParams& p, const dim3& grid, size_t lds, hipStream_t stream) {
+  if (p.group <= 1)
+    decode_valu_kernel<T, D, 1><<<grid, kBlock, lds, stream>>>(p);
+  else if (p.group <= 2)
+    decode_valu_kernel<T, D, 2><<<grid, kBlock, lds, stream>>>(p);
+  else if (p.group <= 4)
+    decode_valu_kernel<T, D, 4><<<grid, kBlock, lds, stream>>>(p);
+  else if (p.group <= 8)
+    decode_valu_kernel<T, D, 8><<<grid, kBlock, lds, stream>>>(p);
+  else
+    decode_valu_kernel<T, D, 16><<<grid, kBlock, lds, stream>>>(p);
 }
 
 template <typename T>
@@ -161,9 +230,9 @@ hipError_t launch_t(const DecodeParams& p, int head_dim, hipStream_t stream) {
   const dim3 grid(decode_grid(p.num_units));
   const size_t lds = merge_lds_bytes(p.group, head_dim) + sizeof(float) * p.group * head_dim;
   if (head_dim == 128)
-    decode_valu_kernel<T, 128><<<grid, kBlock, lds, stream>>>(p);
+    launch_g<T, 128>(p, grid, lds, stream);
   else
-    decode_valu_kernel<T, 64><<<grid, kBlock, lds, stream>>>(p);
+    launch_g<T, 64>(p, grid, lds, stream);
   return hipGetLastError();
 }
 

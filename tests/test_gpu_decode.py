@@ -103,6 +103,8 @@ def test_single_token_context_returns_v_exactly(dtype, D, kernel):
         ([700, 3, 48, 129], 4, 4, 128, "bf16"),      # no grouping
         ([700, 3, 48, 129], 12, 4, 128, "bf16"),     # group of 3
         ([700, 3, 48, 129], 16, 1, 64, "f32"),
+        ([700, 3, 48, 129], 12, 2, 128, "f32"),      # group of 6
+        ([700, 3, 48, 129], 24, 2, 64, "bf16"),      # group of 12
         ([5000, 4097, 2], 8, 1, 128, "bf16"),        # more than 64 pages per wave
     ],
 )
