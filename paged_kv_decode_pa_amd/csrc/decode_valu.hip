@@ -10,7 +10,7 @@
 // d and d+64 and reads those dims' 16 value slots (the V page is stored
 // dim-major, so that is one contiguous row per dim); each token's weight is
 // broadcast from its owner lane with readlane.
-#include "pa_device.hpp"
+#include "split_plan.hpp"
 
 namespace pa {
 namespace {
@@ -76,14 +76,27 @@ __device__ inline float token_max(float m) {
 
 // GB: a bound on the group (1, 2, 4, 8 or 16), so that the per-head state
 // is indexed by unrolled constants only.
-template <typename T, int D, int GB>
+// NC > 0 (split-KV, batches the unit plan covers): unit b is the b-th
+// entry of the split decode's unit list (longest units first, none past a
+// context's end); otherwise the plain grid of (sequence, partition, kv head).
+template <typename T, int D, int GB, int NC>
 __global__ __launch_bounds__(kBlock) void decode_valu_kernel(DecodeParams p) {
   extern __shared__ float smem[];
   constexpr int QD = D / 4;    // key dims per lane
   constexpr int VD = D / 64;   // value dims per lane
   typedef RawPage<T, D> Raw;
   int seq, kvh, part;
-  if (!unit_of(p, blockIdx.x, seq, kvh, part)) return;
+  if constexpr (NC > 0) {
+    const int u = blockIdx.x;
+    if (u >= p.num_units) return;
+    kvh = u % p.num_kv_heads;
+    int seq_pages = 0;
+    if (!split_unit<NC>(p, u / p.num_kv_heads, threadIdx.x & 63, seq, part, seq_pages)) return;
+    seq = __builtin_amdgcn_readfirstlane(seq);
+    part = __builtin_amdgcn_readfirstlane(part);
+  } else {
+    if (!unit_of(p, blockIdx.x, seq, kvh, part)) return;
+  }
   const int L = p.context_lens[seq];
   int lo, hi;
   if (!unit_pages(p, seq, part, L, lo, hi)) {
@@ -209,30 +222,44 @@ __global__ __launch_bounds__(kBlock) void decode_valu_kernel(DecodeParams p) {
     }
   }
   merge_and_store<T, D>(p, lds, seq, kvh, part);
+  // The plan has no units past a length clamped to the block table's width:
+  // the unit of the last partition with tokens writes the empty partials of
+  // the partitions after it that the merge counts.
+  if constexpr (NC > 0) {
+    const int n = min((L + kPage - 1) / kPage, p.max_pages_per_seq);
+    if (hi == n) empty_partials<D>(p, seq, kvh, part + 1, merged_partitions(p, L), threadIdx.x, kBlock);
+  }
 }
 
-template <typename T, int D>
+template <typename T, int D, int NC>
 void launch_g(const DecodeParams& p, const dim3& grid, size_t lds, hipStream_t stream) {
   if (p.group <= 1)
-    decode_valu_kernel<T, D, 1><<<grid, kBlock, lds, stream>>>(p);
+    decode_valu_kernel<T, D, 1, NC><<<grid, kBlock, lds, stream>>>(p);
   else if (p.group <= 2)
-    decode_valu_kernel<T, D, 2><<<grid, kBlock, lds, stream>>>(p);
+    decode_valu_kernel<T, D, 2, NC><<<grid, kBlock, lds, stream>>>(p);
   else if (p.group <= 4)
-    decode_valu_kernel<T, D, 4><<<grid, kBlock, lds, stream>>>(p);
+    decode_valu_kernel<T, D, 4, NC><<<grid, kBlock, lds, stream>>>(p);
   else if (p.group <= 8)
-    decode_valu_kernel<T, D, 8><<<grid, kBlock, lds, stream>>>(p);
+    decode_valu_kernel<T, D, 8, NC><<<grid, kBlock, lds, stream>>>(p);
   else
-    decode_valu_kernel<T, D, 16><<<grid, kBlock, lds, stream>>>(p);
+    decode_valu_kernel<T, D, 16, NC><<<grid, kBlock, lds, stream>>>(p);
 }
 
 template <typename T>
 hipError_t launch_t(const DecodeParams& p, int head_dim, hipStream_t stream) {
   const dim3 grid(decode_grid(p.num_units));
   const size_t lds = merge_lds_bytes(p.group, head_dim) + sizeof(float) * p.group * head_dim;
-  if (head_dim == 128)
-    launch_g<T, 128>(p, grid, lds, stream);
-  else
-    launch_g<T, 64>(p, grid, lds, stream);
+  // The split decode's unit list, when it covers the batch and no other
+  // launch computes some partitions (a shared prefix's).
+  const bool plan = p.pages_per_partition > 0 && p.first_partition == nullptr &&
+                    plan_chunks_for(p.num_seqs) > 0;
+  if (head_dim == 128) {
+    if (plan) launch_g<T, 128, kPlanChunks>(p, grid, lds, stream);
+    else launch_g<T, 128, 0>(p, grid, lds, stream);
+  } else {
+    if (plan) launch_g<T, 64, kPlanChunks>(p, grid, lds, stream);
+    else launch_g<T, 64, 0>(p, grid, lds, stream);
+  }
   return hipGetLastError();
 }
 
