@@ -10,6 +10,8 @@
 // d and d+64 and reads those dims' 16 value slots (the V page is stored
 // dim-major, so that is one contiguous row per dim); each token's weight is
 // broadcast from its owner lane with readlane.
+#include <type_traits>
+
 #include "split_plan.hpp"
 
 namespace pa {
@@ -97,6 +99,12 @@ __global__ __launch_bounds__(kBlock) void decode_valu_kernel(DecodeParams p) {
   } else {
     if (!unit_of(p, blockIdx.x, seq, kvh, part)) return;
   }
+  // Single pass: the snake order by length of the matrix-core single pass
+  // (when the host asks for it), and nontemporal loads for a sequence whose
+  // pages no other sequence reads.
+  bool shared = true;
+  if (NC == 0 && p.pages_per_partition == 0 && p.snake_period > 0)
+    seq = snake_unit_seq_of_batch(p, seq, threadIdx.x & 63, shared);
   const int L = p.context_lens[seq];
   int lo, hi;
   if (!unit_pages(p, seq, part, L, lo, hi)) {
@@ -134,7 +142,8 @@ __global__ __launch_bounds__(kBlock) void decode_valu_kernel(DecodeParams p) {
   // The wave's k-th page (clamped to its last): loads issued unconditionally,
   // so that the compiler counts the loads in flight exactly; an out-of-range
   // id loads page 0 and the page is skipped.
-  auto issue = [&](Raw& r, int k, int& ord, bool& ok) {
+  auto issue = [&](auto nt_tag, Raw& r, int k, int& ord, bool& ok) {
+    constexpr bool NT = decltype(nt_tag)::value;
     const int kk = min(k, n_my - 1);
     ord = lo + w + kk * kWaves;
     const int page = table[ord];
@@ -143,13 +152,13 @@ __global__ __launch_bounds__(kBlock) void decode_valu_kernel(DecodeParams p) {
     const u32x4* ks = reinterpret_cast<const u32x4*>(static_cast<const T*>(p.k_cache) + base +
                                                      t * D + c * QD);
 #pragma unroll
-    for (int i = 0; i < Raw::KQ; ++i) r.k[i] = ks[i];
+    for (int i = 0; i < Raw::KQ; ++i) r.k[i] = NT ? __builtin_nontemporal_load(ks + i) : ks[i];
 #pragma unroll
     for (int vi = 0; vi < VD; ++vi) {
       const u32x4* vs = reinterpret_cast<const u32x4*>(static_cast<const T*>(p.v_cache) + base +
                                                        (lane + 64 * vi) * kPage);
 #pragma unroll
-      for (int i = 0; i < Raw::VQ; ++i) r.v[vi][i] = vs[i];
+      for (int i = 0; i < Raw::VQ; ++i) r.v[vi][i] = NT ? __builtin_nontemporal_load(vs + i) : vs[i];
     }
   };
 
@@ -192,18 +201,23 @@ __global__ __launch_bounds__(kBlock) void decode_valu_kernel(DecodeParams p) {
     }
   };
 
-  // Two pages in flight: page k + 1 loads while page k is computed.
-  if (n_my > 0) {
+  // Two pages in flight: page k + 1 loads while page k is computed (one
+  // instantiation per load policy, so that no load sits under a branch).
+  auto walk = [&](auto nt_tag) {
     Raw r0, r1;
     int o0, o1;
     bool ok0, ok1;
-    issue(r0, 0, o0, ok0);
+    issue(nt_tag, r0, 0, o0, ok0);
     for (int k = 0; k < n_my; k += 2) {
-      issue(r1, k + 1, o1, ok1);
+      issue(nt_tag, r1, k + 1, o1, ok1);
       if (ok0) compute(r0, o0);
-      issue(r0, k + 2, o0, ok0);
+      issue(nt_tag, r0, k + 2, o0, ok0);
       if (ok1) compute(r1, o1);
     }
+  };
+  if (n_my > 0) {
+    if (shared) walk(std::false_type{});
+    else walk(std::true_type{});
   }
 
 #pragma unroll

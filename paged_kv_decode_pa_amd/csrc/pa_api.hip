@@ -169,9 +169,14 @@ int decode_impl(DecodeKernel which, void* out, const void* query, const void* k_
                             new_key, new_value, new_slots, nullptr, false, 0, p, mfma, empty))
     return st;
   if (empty) return PA_OK;
-  if (mfma && partition_size == 0) {
+  if (partition_size == 0) {
+    // The single pass takes its units in the snake order by length.  The
+    // vector kernel does so only when its units outnumber the compute units:
+    // below that the order changes nothing and its length loads cost a round
+    // trip (tiny fp32 batch: 17.4 -> 19.9 us).
     const int cus = device_compute_units();
-    p.snake_period = cus > 0 ? (cus / num_kv_heads > 0 ? cus / num_kv_heads : 1) : 0;
+    if (mfma || int64_t(num_seqs) * num_kv_heads > cus)
+      p.snake_period = cus > 0 ? (cus / num_kv_heads > 0 ? cus / num_kv_heads : 1) : 0;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = dtype == PA_DTYPE_BF16;
