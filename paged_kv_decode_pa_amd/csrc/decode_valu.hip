@@ -4,7 +4,9 @@
 //
 // Per page and kv head, lane (t, c) = (lane / 4, lane % 4) holds token t's
 // key slice [c*D/4, (c+1)*D/4) and forms partial dots against the query
-// group (kept in LDS as fp32); a quad butterfly (DPP) finishes each score.
+// group (kept in LDS: fp32, or the bf16 pairs as stored, which bf16 keys
+// take two at a time with v_dot2); a quad butterfly (DPP) finishes each
+// score.
 // The page maximum per head comes from DPP mirrors and gfx950's lane-swap
 // instructions, without an LDS round trip.  For P.V, lane d owns output dims
 // d and d+64 and reads those dims' 16 value slots (the V page is stored
@@ -18,6 +20,7 @@ namespace pa {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 template <typename T>
 __device__ inline float load_one(const void* base, size_t i) {
@@ -116,10 +119,17 @@ __global__ __launch_bounds__(kBlock) void decode_valu_kernel(DecodeParams p) {
   }
   const int G = p.group;
   MergeLds lds(smem);
-  float* qs = smem + merge_lds_bytes(G, D) / sizeof(float);  // [G][D] fp32
+  float* qs = smem + merge_lds_bytes(G, D) / sizeof(float);  // [G][D] fp32 (bf16: pairs)
 
-  for (int idx = threadIdx.x; idx < G * D; idx += kBlock)
-    qs[idx] = load_one<T>(p.query, (size_t(seq) * p.num_q_heads + kvh * G) * D + idx);
+  if constexpr (sizeof(T) == 4) {
+    for (int idx = threadIdx.x; idx < G * D; idx += kBlock)
+      qs[idx] = load_one<T>(p.query, (size_t(seq) * p.num_q_heads + kvh * G) * D + idx);
+  } else {  // bf16 pairs, as stored
+    const uint32_t* qg = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.query) +
+                                                         (size_t(seq) * p.num_q_heads + kvh * G) * D);
+    for (int idx = threadIdx.x; idx < G * D / 2; idx += kBlock)
+      reinterpret_cast<uint32_t*>(qs)[idx] = qg[idx];
+  }
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
@@ -164,8 +174,8 @@ __global__ __launch_bounds__(kBlock) void decode_valu_kernel(DecodeParams p) {
 
   auto compute = [&](const Raw& r, int ord) {
     const int valid = L - ord * kPage;
-    float kv[QD];
-    widen<T, QD>(r.k, kv);
+    float kv[sizeof(T) == 4 ? QD : 1];
+    if constexpr (sizeof(T) == 4) widen<T, QD>(r.k, kv);
     float vv[VD][kPage];
 #pragma unroll
     for (int vi = 0; vi < VD; ++vi) {
@@ -179,10 +189,28 @@ __global__ __launch_bounds__(kBlock) void decode_valu_kernel(DecodeParams p) {
 #pragma unroll
     for (int h = 0; h < GB; ++h) {
       if (h < G) {  // uniform
-        const float* qh = qs + h * D + c * QD;
         float part_dot = 0.f;
+        if constexpr (sizeof(T) == 4) {
+          const float* qh = qs + h * D + c * QD;
 #pragma unroll
-        for (int e = 0; e < QD; ++e) part_dot = fmaf(qh[e], kv[e], part_dot);
+          for (int e = 0; e < QD; ++e) part_dot = fmaf(qh[e], kv[e], part_dot);
+        } else {
+          // bf16 keys and query: two products per instruction (v_dot2), no
+          // widening.  The words go through plain variables: a bit_cast of
+          // the vector element itself compiled to element 0 for every f.
+          const uint32_t* qh = reinterpret_cast<const uint32_t*>(qs) + h * (D / 2) + c * (QD / 2);
+#pragma unroll
+          for (int e = 0; e < QD / 8; ++e)
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+            {
+              const uint32_t kw = r.k[e][f];
+              const uint32_t qw = qh[4 * e + f];
+              part_dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, kw),
+                                                         __builtin_bit_cast(bf16x2_t, qw), part_dot,
+                                                         false);
+            }
+        }
         const float s2 = (t < valid) ? quad_sum(part_dot) * p.scale_log2 : -INFINITY;
         const float m_new = fmaxf(m_run[h], token_max(s2));
         const float alpha = __builtin_amdgcn_exp2f(m_run[h] - m_new);
