@@ -11,7 +11,9 @@
 // instructions, without an LDS round trip.  For P.V, lane d owns output dims
 // d and d+64 and reads those dims' 16 value slots (the V page is stored
 // dim-major, so that is one contiguous row per dim); each token's weight is
-// broadcast from its owner lane with readlane.
+// broadcast from its owner lane with readlane.  For bf16 pools P is rounded
+// to bf16 and two tokens go into one v_dot2 with their value words as loaded
+// (the denominator sums the same rounded P); fp32 pools keep fp32 P.
 #include <type_traits>
 
 #include "split_plan.hpp"
@@ -176,14 +178,29 @@ __global__ __launch_bounds__(kBlock) void decode_valu_kernel(DecodeParams p) {
     const int valid = L - ord * kPage;
     float kv[sizeof(T) == 4 ? QD : 1];
     if constexpr (sizeof(T) == 4) widen<T, QD>(r.k, kv);
-    float vv[VD][kPage];
+    // fp32: the value rows widened; bf16: kept as words of two tokens.
+    float vv[VD][sizeof(T) == 4 ? kPage : 1];
+    uint32_t vw[VD][sizeof(T) == 4 ? 1 : kPage / 2];
 #pragma unroll
     for (int vi = 0; vi < VD; ++vi) {
-      widen<T, kPage>(r.v[vi], vv[vi]);
-      if (valid < kPage) {
+      if constexpr (sizeof(T) == 4) {
+        widen<T, kPage>(r.v[vi], vv[vi]);
+        if (valid < kPage) {
 #pragma unroll
-        for (int tt = 0; tt < kPage; ++tt)
-          if (tt >= valid) vv[vi][tt] = 0.f;  // unwritten slots may hold NaN
+          for (int tt = 0; tt < kPage; ++tt)
+            if (tt >= valid) vv[vi][tt] = 0.f;  // unwritten slots may hold NaN
+        }
+      } else {
+#pragma unroll
+        for (int w2 = 0; w2 < kPage / 2; ++w2) {
+          const uint32_t x = r.v[vi][w2 / 4][w2 % 4];
+          vw[vi][w2] = x;
+        }
+        if (valid < kPage) {
+#pragma unroll
+          for (int w2 = 0; w2 < kPage / 2; ++w2)
+            vw[vi][w2] &= (2 * w2 < valid ? 0x0000ffffu : 0u) | (2 * w2 + 1 < valid ? 0xffff0000u : 0u);
+        }
       }
     }
 #pragma unroll
@@ -216,14 +233,34 @@ __global__ __launch_bounds__(kBlock) void decode_valu_kernel(DecodeParams p) {
         const float alpha = __builtin_amdgcn_exp2f(m_run[h] - m_new);
         m_run[h] = m_new;
         const float pe = __builtin_amdgcn_exp2f(s2 - m_new);
-        l_run[h] = l_run[h] * alpha + (c == 0 ? pe : 0.f);
 #pragma unroll
         for (int vi = 0; vi < VD; ++vi) acc[h][vi] *= alpha;
+        if constexpr (sizeof(T) == 4) {
+          l_run[h] = l_run[h] * alpha + (c == 0 ? pe : 0.f);
 #pragma unroll
-        for (int tt = 0; tt < kPage; ++tt) {
-          const float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pe), 4 * tt));
+          for (int tt = 0; tt < kPage; ++tt) {
+            const float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pe), 4 * tt));
 #pragma unroll
-          for (int vi = 0; vi < VD; ++vi) acc[h][vi] = fmaf(wt, vv[vi][tt], acc[h][vi]);
+            for (int vi = 0; vi < VD; ++vi) acc[h][vi] = fmaf(wt, vv[vi][tt], acc[h][vi]);
+          }
+        } else {
+          // bf16 V: P rounded to bf16 (nearest even), two tokens per v_dot2;
+          // the denominator sums the same rounded P.
+          const uint32_t pb = f32_to_bf16(pe);
+          l_run[h] = l_run[h] * alpha + (c == 0 ? __uint_as_float(pb << 16) : 0.f);
+#pragma unroll
+          for (int w2 = 0; w2 < kPage / 2; ++w2) {
+            const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(pb), 8 * w2));
+            const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(pb), 8 * w2 + 4));
+            const uint32_t pw = lo | (hi << 16);
+#pragma unroll
+            for (int vi = 0; vi < VD; ++vi) {
+              const uint32_t x = vw[vi][w2];
+              acc[h][vi] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x),
+                                                           __builtin_bit_cast(bf16x2_t, pw),
+                                                           acc[h][vi], false);
+            }
+          }
         }
       }
     }
