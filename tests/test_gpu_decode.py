@@ -219,16 +219,34 @@ def test_split_plan_with_empty_and_ragged_contexts():
                 assert np.abs(out[b] - ref[b]).max() <= TOL["bf16"], (ps, b)
 
 
-def test_split_beyond_planned_batch_size():
-    """More than 1024 sequences: the split kernel falls back to the plain grid."""
-    say("[decode] 1100-sequence batch")
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_split_beyond_planned_batch_size(kernel):
+    """More than 1024 sequences: the split kernels fall back to the plain grid
+    and the single passes to batch order."""
+    say(f"[decode] 1100-sequence batch {kernel}")
     rng = np.random.default_rng(5)
     lens = rng.integers(1, 80, size=1100).tolist()
     wl = make_custom_workload(lens, num_q_heads=8, num_kv_heads=1, head_dim=128, seed=6)
     ref = oracle_reference(wl)
     dev = DeviceWorkload(wl)
     for ps in (0, 32):
-        assert max_err(dev.decode(ps), ref) <= TOL["bf16"], ps
+        assert max_err(dev.decode(ps, kernel), ref) <= TOL["bf16"], ps
+
+
+@pytest.mark.parametrize("n", [300, 1100])
+def test_fp32_batches_in_length_order_and_past_the_plan(n):
+    """fp32 (the vector kernel): a single pass with more units than compute
+    units takes the length order; split partitions take the unit plan up to
+    1024 sequences and the plain grid past it."""
+    say(f"[decode] fp32 batch of {n}")
+    rng = np.random.default_rng(n)
+    lens = rng.integers(1, 300, size=n).tolist()
+    wl = make_custom_workload(lens, num_q_heads=8, num_kv_heads=2, head_dim=64, dtype="f32",
+                              seed=n)
+    ref = oracle_reference(wl)
+    dev = DeviceWorkload(wl)
+    for ps in (0, 64):
+        assert max_err(dev.decode(ps), ref) <= TOL["f32"], ps
 
 
 @pytest.mark.parametrize("B", [48, 200, 300])
