@@ -22,12 +22,6 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-template <typename T>
-__device__ inline float load_one(const void* base, size_t i) {
-  if constexpr (sizeof(T) == 4) return static_cast<const float*>(base)[i];
-  else return bf16_to_f32(static_cast<const uint16_t*>(base)[i]);
-}
-
 // One page's K slice and V rows of a lane, as loaded (bf16 or fp32 bits).
 template <typename T, int D>
 struct RawPage {
@@ -37,22 +31,13 @@ struct RawPage {
   u32x4 v[D / 64][VQ];
 };
 
-template <typename T, int n>
-__device__ inline void widen(const u32x4* src, float* dst) {
-  if constexpr (sizeof(T) == 4) {
+// n fp32 values from their loaded words.
+template <int n>
+__device__ inline void words_to_f32(const u32x4* src, float* dst) {
 #pragma unroll
-    for (int i = 0; i < n / 4; ++i)
+  for (int i = 0; i < n / 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dst[4 * i + e] = __uint_as_float(src[i][e]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < n / 8; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        dst[8 * i + 2 * e] = __uint_as_float(src[i][e] << 16);
-        dst[8 * i + 2 * e + 1] = __uint_as_float(src[i][e] & 0xffff0000u);
-      }
-  }
+    for (int e = 0; e < 4; ++e) dst[4 * i + e] = __uint_as_float(src[i][e]);
 }
 
 // The sum over a lane quad (a token's four key slices), in the order of two
@@ -124,7 +109,7 @@ __global__ __launch_bounds__(kBlock) void decode_valu_kernel(DecodeParams p) {
 
   if constexpr (sizeof(T) == 4) {
     for (int idx = threadIdx.x; idx < G * D; idx += kBlock)
-      qs[idx] = load_one<T>(p.query, (size_t(seq) * p.num_q_heads + kvh * G) * D + idx);
+      qs[idx] = static_cast<const float*>(p.query)[(size_t(seq) * p.num_q_heads + kvh * G) * D + idx];
   } else {  // bf16 pairs, as stored
     const uint32_t* qg = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.query) +
                                                          (size_t(seq) * p.num_q_heads + kvh * G) * D);
@@ -175,14 +160,14 @@ __global__ __launch_bounds__(kBlock) void decode_valu_kernel(DecodeParams p) {
   auto compute = [&](const Raw& r, int ord) {
     const int valid = L - ord * kPage;
     float kv[sizeof(T) == 4 ? QD : 1];
-    if constexpr (sizeof(T) == 4) widen<T, QD>(r.k, kv);
+    if constexpr (sizeof(T) == 4) words_to_f32<QD>(r.k, kv);
     // fp32: the value rows widened; bf16: kept as words of two tokens.
     float vv[VD][sizeof(T) == 4 ? kPage : 1];
     uint32_t vw[VD][sizeof(T) == 4 ? 1 : kPage / 2];
 #pragma unroll
     for (int vi = 0; vi < VD; ++vi) {
       if constexpr (sizeof(T) == 4) {
-        widen<T, kPage>(r.v[vi], vv[vi]);
+        words_to_f32<kPage>(r.v[vi], vv[vi]);
         if (valid < kPage) {
 #pragma unroll
           for (int tt = 0; tt < kPage; ++tt)
