@@ -353,10 +353,11 @@ int pa_decode_cascade(const void* query, const void* key, const void* value,
  * pa_decode_valu — pa_decode with the vector-ALU kernel forced.
  *
  * Same arguments, layouts, results contract and errors as pa_decode.  For
- * bf16, pa_decode runs the QK^T and P.V products on the matrix cores with P
- * rounded to bf16; this variant keeps every product in fp32 on the vector
- * ALU.  It exists to measure and cross-check the two designs; fp32 pa_decode
- * already uses it.
+ * bf16, pa_decode runs the QK^T and P.V products on the matrix cores; this
+ * variant runs them on the vector ALU (bf16 pairs with fp32 accumulation,
+ * P rounded to bf16 as on the matrix cores).  It exists to measure and
+ * cross-check the two designs; fp32 pa_decode already uses it, with every
+ * product in fp32.
  */
 int pa_decode_valu(void* out, const void* query, const void* k_cache, const void* v_cache,
                    const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
